@@ -1,0 +1,222 @@
+"""ragattn: ragged, batched, masked GQA attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libragattn.so`` (declared in
+``include/ragattn.h``). These functions only marshal arguments: they check
+tensor dtypes/devices, read sizes from tensor shapes, allocate ``out``/``lse``
+when the caller does not pass them, and call the C entry point of the same
+name on the current HIP stream. Every step of the attention runs in the HIP
+kernels; there is no fallback path. If the library has not been built (see
+``attention_ragged_gqa_amd.build``) the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "RagAttnError",
+    "library",
+    "lib_path",
+    "EXPORTED_SYMBOLS",
+    "ra_tree_attn",
+    "ra_paged_attn",
+    "ra_paged_kv_append",
+    "ra_last_error",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libragattn.so"
+
+EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_paged_kv_append", "ra_last_error")
+
+RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
+RA_F16, RA_BF16 = 0, 1
+_STATUS = {RA_EINVAL: "RA_EINVAL", RA_EUNSUPPORTED: "RA_EUNSUPPORTED", RA_EHIP: "RA_EHIP"}
+_DTYPES = {torch.float16: RA_F16, torch.bfloat16: RA_BF16}
+
+
+class RagAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.environ.get("RAGATTN_LIB", os.path.join(_PKG_DIR, LIB_NAME))
+
+
+def library() -> ctypes.CDLL:
+    """Load libragattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "%s not found: build it with `python -m attention_ragged_gqa_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    lib.ra_tree_attn.restype = i32
+    lib.ra_tree_attn.argtypes = [vp] * 10 + [i32] * 8 + [i32, f32, f32, f32, vp]
+    lib.ra_paged_attn.restype = i32
+    lib.ra_paged_attn.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
+                                  + [i32, i32, f32, f32, f32, vp])
+    lib.ra_paged_kv_append.restype = i32
+    lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
+    lib.ra_last_error.restype = ctypes.c_char_p
+    lib.ra_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def ra_last_error() -> str:
+    return library().ra_last_error().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name: str, t: Optional[torch.Tensor], dtype=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor (got %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+
+
+def _stream(device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _raise(status: int):
+    if status != RA_OK:
+        raise RagAttnError(status, ra_last_error())
+
+
+def _out_lse(q, out, lse):
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    _check_dev("out", out, q.dtype, q.device)
+    _check_dev("lse", lse, torch.float32, q.device)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must be shaped like q and lse like q[:, :, 0]")
+    return out, lse
+
+
+def ra_tree_attn(q, q_indptr, k, v, kv_indptr, q_rope_position, mn_indptr, tree_mask,
+                 out=None, lse=None, rotary_mode: int = 0, rope_scale: float = 1.0,
+                 rope_theta: float = 1e4, sm_scale: Optional[float] = None, stream=None):
+    """Batched tree attention over contiguous KV (C: ra_tree_attn).
+
+    q [total_q, h_q, d], k/v [total_kv, h_kv, d] (fp16/bf16); q_indptr,
+    kv_indptr, mn_indptr [b+1], q_rope_position [total_q] (or None when
+    rotary_mode == 0), tree_mask [n, 2] int32. Returns (out, lse)."""
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("kv_indptr", kv_indptr), ("mn_indptr", mn_indptr),
+                    ("q_rope_position", q_rope_position), ("tree_mask", tree_mask)):
+        _check_dev(name, t, i32, dev)
+    out, lse = _out_lse(q, out, lse)
+    total_q, h_q, d = q.shape
+    total_kv, h_kv = k.shape[0], k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    st = library().ra_tree_attn(
+        _ptr(q), _ptr(q_indptr), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(q_rope_position),
+        _ptr(mn_indptr), _ptr(tree_mask), _ptr(out), _ptr(lse),
+        q_indptr.numel() - 1, total_q, total_kv, tree_mask.shape[0], h_q, h_kv, d,
+        _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale, _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info,
+                  sliding_window: int = 0, k_rope_pos_offset=None, q_rope_position=None,
+                  tree_order_indptr=None, tree_order=None, causal: int = 1, out=None, lse=None,
+                  rotary_mode: int = 0, rope_scale: float = 1.0, rope_theta: float = 1e4,
+                  sm_scale: Optional[float] = None, stream=None):
+    """Ragged prefill / tree attention over a paged KV cache (C: ra_paged_attn).
+
+    pages [num_pages, 2, h_kv, 16, d]; length_info [b] or [3, b] int32.
+    Returns (out, lse)."""
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    _check_dev("pages", pages, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("page_indptr", page_indptr),
+                    ("page_values", page_values), ("length_info", length_info),
+                    ("k_rope_pos_offset", k_rope_pos_offset), ("q_rope_position", q_rope_position),
+                    ("tree_order_indptr", tree_order_indptr), ("tree_order", tree_order)):
+        _check_dev(name, t, i32, dev)
+    if pages.dim() != 5 or pages.shape[1] != 2:
+        raise ValueError("pages must be [num_pages, 2, h_kv, page_size, d]")
+    out, lse = _out_lse(q, out, lse)
+    total_q, h_q, d = q.shape
+    num_pages, _, h_kv, page_size, dp = pages.shape
+    if dp != d:
+        raise ValueError("pages head_dim %d != q head_dim %d" % (dp, d))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    tree_size = 0 if tree_order is None else tree_order.shape[0]
+    st = library().ra_paged_attn(
+        _ptr(q), _ptr(q_indptr), _ptr(pages), _ptr(page_indptr), _ptr(page_values),
+        _ptr(length_info), int(sliding_window), _ptr(k_rope_pos_offset), _ptr(q_rope_position),
+        _ptr(tree_order_indptr), _ptr(tree_order), int(causal), _ptr(out), _ptr(lse),
+        q_indptr.numel() - 1, total_q, num_pages, page_values.numel(), tree_size, page_size,
+        h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
+        _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_paged_kv_append(k, v, append_indptr, append_start, rope_position, page_indptr,
+                       page_values, pages, rope_scale: float = 1.0, rope_theta: float = 1e4,
+                       stream=None):
+    """Write tokens k/v [n, h_kv, d] into ``pages`` in place, rotating K at
+    rope_position when it is given (C: ra_paged_kv_append)."""
+    dev = pages.device
+    i32 = torch.int32
+    _check_dev("pages", pages, None, dev)
+    if pages.dtype not in _DTYPES:
+        raise TypeError("pages must be fp16 or bf16")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, pages.dtype, dev)
+    for name, t in (("append_indptr", append_indptr), ("append_start", append_start),
+                    ("rope_position", rope_position), ("page_indptr", page_indptr),
+                    ("page_values", page_values)):
+        _check_dev(name, t, i32, dev)
+    num_pages, _, h_kv, page_size, d = pages.shape
+    st = library().ra_paged_kv_append(
+        _ptr(k), _ptr(v), _ptr(append_indptr), _ptr(append_start), _ptr(rope_position),
+        _ptr(page_indptr), _ptr(page_values), _ptr(pages), append_indptr.numel() - 1,
+        k.shape[0], num_pages, page_values.numel(), page_size, h_kv, d, _DTYPES[pages.dtype],
+        rope_scale, rope_theta, _stream(dev, stream))
+    _raise(st)
+    return pages

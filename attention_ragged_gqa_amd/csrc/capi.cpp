@@ -1,0 +1,212 @@
+// C ABI of libragattn.so: argument validation, error reporting and dispatch.
+// Nothing here touches device memory; every call launches at most one kernel
+// on the caller's stream and returns without synchronising.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "ra_internal.h"
+#include "../../include/ragattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ra_status ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+ra_status check_common(const void* q, const void* q_indptr, const void* out, const void* lse,
+                       int32_t batch, int32_t total_q, int32_t h_q, int32_t h_kv,
+                       int32_t head_dim, ra_dtype dtype, int32_t rotary_mode, float sm_scale) {
+  if (batch < 0 || total_q < 0) return fail(RA_EINVAL, "negative batch (%d) or total_q (%d)", batch, total_q);
+  if (batch > 0 && q_indptr == nullptr) return fail(RA_EINVAL, "q_indptr is NULL");
+  if (total_q > 0 && (q == nullptr || out == nullptr || lse == nullptr))
+    return fail(RA_EINVAL, "q, out and lse must be non-NULL");
+  if (h_q <= 0 || h_kv <= 0) return fail(RA_EINVAL, "h_q (%d) and h_kv (%d) must be positive", h_q, h_kv);
+  if (h_q % h_kv != 0) return fail(RA_EINVAL, "h_q (%d) is not a multiple of h_kv (%d)", h_q, h_kv);
+  if (rotary_mode != 0 && rotary_mode != 1) return fail(RA_EINVAL, "rotary_mode must be 0 or 1, got %d", rotary_mode);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(RA_EINVAL, "sm_scale must be finite and > 0");
+  if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported (fp16=0, bf16=1)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  return RA_OK;
+}
+
+ra_status check_rope(int32_t rotary_mode, float rope_scale, float rope_theta) {
+  if (rotary_mode == 1 && (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !std::isfinite(rope_scale)))
+    return fail(RA_EINVAL, "rope_theta must be finite and > 0, rope_scale finite");
+  return RA_OK;
+}
+
+ra_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(RA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_err; }
+
+ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, const void* v,
+                       const int32_t* kv_indptr, const int32_t* q_rope_position,
+                       const int32_t* mn_indptr, const int32_t* tree_mask, void* out, float* lse,
+                       int32_t batch, int32_t total_q, int32_t total_kv, int32_t tree_size,
+                       int32_t h_q, int32_t h_kv, int32_t head_dim, ra_dtype dtype,
+                       int32_t rotary_mode, float rope_scale, float rope_theta, float sm_scale,
+                       hipStream_t stream) {
+  ra_status st = check_common(q, q_indptr, out, lse, batch, total_q, h_q, h_kv, head_dim, dtype,
+                              rotary_mode, sm_scale);
+  if (st != RA_OK) return st;
+  if ((st = check_rope(rotary_mode, rope_scale, rope_theta)) != RA_OK) return st;
+  if (total_kv < 0 || tree_size < 0) return fail(RA_EINVAL, "negative total_kv or tree_size");
+  if (batch > 0 && (kv_indptr == nullptr || mn_indptr == nullptr))
+    return fail(RA_EINVAL, "kv_indptr and mn_indptr must be non-NULL");
+  if (total_kv > 0 && (k == nullptr || v == nullptr)) return fail(RA_EINVAL, "k and v must be non-NULL");
+  if (tree_size > 0 && tree_mask == nullptr) return fail(RA_EINVAL, "tree_mask is NULL");
+  if (rotary_mode == 1 && (total_q > 0 || total_kv > 0) && q_rope_position == nullptr)
+    return fail(RA_EINVAL, "rotary_mode 1 needs q_rope_position");
+  if (rotary_mode == 1 && total_kv > total_q)
+    return fail(RA_EINVAL, "rotary_mode 1 rotates K row r at q_rope_position[r]: total_kv (%d) must not exceed total_q (%d)",
+                total_kv, total_q);
+  if (batch == 0 || total_q == 0) return ok();
+
+  ra::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_indptr = q_indptr;
+  p.out = out;
+  p.lse = lse;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.kv_indptr = kv_indptr;
+  p.tree_indptr = mn_indptr;
+  p.tree_order = tree_mask;
+  p.q_rope_position = q_rope_position;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_kv = total_kv;
+  p.tree_size = tree_size;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.group = h_q / h_kv;
+  p.rope_q = rotary_mode == 1;
+  p.rope_k = rotary_mode == 1;
+  p.rope_scale = rope_scale;
+  p.log2_theta = rotary_mode == 1 ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kContiguous, ra::kMaskTree, stream));
+}
+
+ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* pages,
+                        const int32_t* page_indptr, const int32_t* page_values,
+                        const int32_t* length_info, int32_t sliding_window,
+                        const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
+                        const int32_t* tree_order_indptr, const int32_t* tree_order,
+                        int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
+                        int32_t num_pages, int32_t nnz_pages, int32_t tree_size,
+                        int32_t page_size, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                        ra_dtype dtype, int32_t rotary_mode, float rope_scale, float rope_theta,
+                        float sm_scale, hipStream_t stream) {
+  ra_status st = check_common(q, q_indptr, out, lse, batch, total_q, h_q, h_kv, head_dim, dtype,
+                              rotary_mode, sm_scale);
+  if (st != RA_OK) return st;
+  if ((st = check_rope(rotary_mode, rope_scale, rope_theta)) != RA_OK) return st;
+  if (page_size != 16) return fail(RA_EUNSUPPORTED, "page_size %d not supported (16)", page_size);
+  if (num_pages < 0 || nnz_pages < 0 || tree_size < 0) return fail(RA_EINVAL, "negative num_pages, nnz_pages or tree_size");
+  if (sliding_window != 0 && sliding_window != 1) return fail(RA_EINVAL, "sliding_window must be 0 or 1");
+  if (batch > 0 && (page_indptr == nullptr || length_info == nullptr))
+    return fail(RA_EINVAL, "page_indptr and length_info must be non-NULL");
+  if (nnz_pages > 0 && page_values == nullptr) return fail(RA_EINVAL, "page_values is NULL");
+  if (num_pages > 0 && pages == nullptr) return fail(RA_EINVAL, "pages is NULL");
+  const bool tree = tree_order != nullptr || tree_order_indptr != nullptr;
+  if (tree && tree_order_indptr == nullptr) return fail(RA_EINVAL, "tree_order given without tree_order_indptr");
+  if (tree && tree_size > 0 && tree_order == nullptr) return fail(RA_EINVAL, "tree_order is NULL");
+  if (tree && sliding_window) return fail(RA_EUNSUPPORTED, "sliding window with a tree mask is not supported");
+  if (rotary_mode == 1 && total_q > 0 && q_rope_position == nullptr)
+    return fail(RA_EINVAL, "rotary_mode 1 needs q_rope_position");
+  if (batch == 0 || total_q == 0) return ok();
+
+  ra::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_indptr = q_indptr;
+  p.out = out;
+  p.lse = lse;
+  p.pages = static_cast<const uint16_t*>(pages);
+  p.page_indptr = page_indptr;
+  p.page_values = page_values;
+  p.length_info = length_info;
+  p.k_rope_pos_offset = k_rope_pos_offset;
+  p.tree_indptr = tree_order_indptr;
+  p.tree_order = tree_order;
+  p.q_rope_position = q_rope_position;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.tree_size = tree ? tree_size : 0;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.group = h_q / h_kv;
+  p.num_pages = num_pages;
+  p.nnz_pages = nnz_pages;
+  p.sliding = sliding_window;
+  p.causal = causal != 0;
+  p.rope_q = rotary_mode == 1;
+  p.rope_k = rotary_mode == 1 && k_rope_pos_offset != nullptr;
+  p.rope_scale = rope_scale;
+  p.log2_theta = rotary_mode == 1 ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kPaged,
+                                  tree ? ra::kMaskTree : ra::kMaskCausal, stream));
+}
+
+ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append_indptr,
+                             const int32_t* append_start, const int32_t* rope_position,
+                             const int32_t* page_indptr, const int32_t* page_values, void* pages,
+                             int32_t batch, int32_t n_tokens, int32_t num_pages,
+                             int32_t nnz_pages, int32_t page_size, int32_t h_kv,
+                             int32_t head_dim, ra_dtype dtype, float rope_scale,
+                             float rope_theta, hipStream_t stream) {
+  if (batch < 0 || n_tokens < 0 || num_pages < 0 || nnz_pages < 0)
+    return fail(RA_EINVAL, "negative size argument");
+  if (n_tokens > 0 && batch == 0) return fail(RA_EINVAL, "n_tokens > 0 needs batch > 0");
+  if (h_kv <= 0) return fail(RA_EINVAL, "h_kv must be positive");
+  if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported", (int)dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  if (page_size != 16) return fail(RA_EUNSUPPORTED, "page_size %d not supported (16)", page_size);
+  if (n_tokens == 0) return ok();
+  if (k == nullptr || v == nullptr || append_indptr == nullptr || append_start == nullptr ||
+      page_indptr == nullptr || pages == nullptr || (nnz_pages > 0 && page_values == nullptr))
+    return fail(RA_EINVAL, "a required pointer is NULL");
+  if (rope_position != nullptr && (!(rope_theta > 0.f) || !std::isfinite(rope_theta) || !std::isfinite(rope_scale)))
+    return fail(RA_EINVAL, "rope_theta must be finite and > 0, rope_scale finite");
+
+  ra::AppendParams p{};
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.append_indptr = append_indptr;
+  p.append_start = append_start;
+  p.rope_position = rope_position;
+  p.page_indptr = page_indptr;
+  p.page_values = page_values;
+  p.pages = static_cast<uint16_t*>(pages);
+  p.batch = batch;
+  p.n_tokens = n_tokens;
+  p.num_pages = num_pages;
+  p.nnz_pages = nnz_pages;
+  p.h_kv = h_kv;
+  p.rope_scale = rope_scale;
+  p.log2_theta = rope_position ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  return launched(ra::launch_append(p, dtype == RA_BF16, head_dim, stream));
+}
+
+}  // extern "C"

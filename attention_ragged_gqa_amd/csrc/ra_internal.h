@@ -1,0 +1,66 @@
+// Internal interface between the C ABI (capi.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Packed query rows per work item (4 waves x 32 rows) and keys per KV tile.
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+
+enum KvLayout { kContiguous = 0, kPaged = 1 };
+enum MaskKind { kMaskCausal = 0, kMaskTree = 1 };  // kMaskCausal also covers "no mask"
+
+// One kernel launch. All pointers are device pointers.
+struct AttnParams {
+  const uint16_t* q;
+  const int32_t* q_indptr;
+  void* out;
+  float* lse;
+  // contiguous KV
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* kv_indptr;
+  // paged KV
+  const uint16_t* pages;
+  const int32_t* page_indptr;
+  const int32_t* page_values;
+  const int32_t* length_info;
+  const int32_t* k_rope_pos_offset;
+  // tree mask (mn_indptr / tree_mask, or tree_order_indptr / tree_order)
+  const int32_t* tree_indptr;
+  const int32_t* tree_order;
+  const int32_t* q_rope_position;
+  int32_t batch, total_q, total_kv, tree_size;
+  int32_t h_q, h_kv, group;
+  int32_t num_pages, nnz_pages;
+  int32_t sliding, causal;
+  int32_t rope_q, rope_k;  // 0/1
+  float rope_scale;
+  float sm_scale_log2;     // sm_scale * log2(e)
+  double log2_theta;
+};
+
+struct AppendParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* append_indptr;
+  const int32_t* append_start;
+  const int32_t* rope_position;
+  const int32_t* page_indptr;
+  const int32_t* page_values;
+  uint16_t* pages;
+  int32_t batch, n_tokens, num_pages, nnz_pages, h_kv;
+  float rope_scale;
+  double log2_theta;
+};
+
+// Launchers (attn_fwd.hip / kv_append.hip). Return the hipError_t of the launch.
+hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
+                       MaskKind mask, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, int is_bf16, int head_dim, hipStream_t stream);
+
+}  // namespace ra

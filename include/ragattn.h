@@ -1,0 +1,151 @@
+/*
+ * ragattn: ragged, batched, masked grouped-query attention for MI355X (gfx950).
+ *
+ * C ABI of libragattn.so. Every entry point launches asynchronously on the
+ * caller's HIP stream, never synchronises, allocates no device memory and
+ * keeps no state between calls. Pointers are caller-owned device memory
+ * unless stated otherwise; inputs are read-only. Index arrays are int32.
+ *
+ * Operation defined by the TVM pages (cited by page and section):
+ *   page "relax/frontend/nn/llm/_kernel_common.py": _rope, _causal_mask,
+ *     _get_kv_chunk_len, _get_seq_offset and the prefill macros
+ *     (compute_s_gemm, softmax_update_causal, compute_o_gemm,
+ *     paged_store_output_lse);
+ *   page "relax/frontend/nn/llm/tree_attn.py": _check_tree_order, the
+ *     tree_attn operator (contiguous KV) and tree_attn_with_paged_kv_cache.
+ *
+ * For every query token i of sequence b and query head h (KV head
+ * h / (h_q / h_kv)) over the visible KV columns j of that sequence:
+ *   s_j = sm_scale * sum_t q[i,h,t] * k[j,kvh,t]
+ *   out[i,h,:] = sum_j softmax(s)_j * v[j,kvh,:]          (stored in dtype)
+ *   lse[i,h]   = log2(sum_j exp(s_j))                      (float32, base 2)
+ * A row with no visible column gets out = 0 and lse = -inf.
+ *
+ * Layouts (row-major):
+ *   q, out     [total_q, h_q, head_dim]    fp16 or bf16
+ *   lse        [total_q, h_q]              float32
+ *   k, v       [total_kv, h_kv, head_dim]  (contiguous KV)
+ *   pages      [num_pages, 2, h_kv, page_size, head_dim], slot 0 = K, 1 = V
+ *   tree masks [n, 2] rows of (enter, exit): DFS pre-order index and
+ *              pre-order index + subtree size of each tree node.
+ *
+ * Index arrays must be consistent with the sizes passed (indptr arrays
+ * non-decreasing, entries inside their arrays). The kernels bound every
+ * access they derive from them by the sizes given: a row, page or tree entry
+ * outside its array is read as zero / not visible rather than dereferenced.
+ */
+#ifndef RAGATTN_H
+#define RAGATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_EINVAL = -1,        /* bad argument: null pointer, negative size, h_q % h_kv != 0, ... */
+  RA_EUNSUPPORTED = -2,  /* valid but not built: head_dim, dtype, page_size, combination */
+  RA_EHIP = -3           /* a HIP launch error (message from hipGetErrorString) */
+} ra_status;
+
+typedef enum { RA_F16 = 0, RA_BF16 = 1 } ra_dtype;
+
+/*
+ * Batched tree attention over contiguous KV ("tree_attn.py" page: tree_attn,
+ * the batch_tree_attn kernel and _check_tree_order).
+ *
+ * Sequence b owns query rows [q_indptr[b], q_indptr[b+1]) and KV rows
+ * [kv_indptr[b], kv_indptr[b+1]); its tree occupies mask rows
+ * [mn_indptr[b], mn_indptr[b+1]) and its nodes are the last
+ * tree_len = mn_indptr[b+1] - mn_indptr[b] KV columns. Column j is visible to
+ * query row i iff j < kv_len and (j < kv_len - tree_len, or with
+ * c = i + tree_len - qo_len and p = j - (kv_len - tree_len):
+ * tree_mask[c].enter in [tree_mask[p].enter, tree_mask[p].exit)).
+ *
+ * rotary_mode: 0 = no rotation; 1 = rotate-half RoPE inside the kernel, q row
+ *   r at position q_rope_position[r] and K row r at q_rope_position[r] (the
+ *   page's kernels index K positions with the same array; KV rows and query
+ *   rows coincide in this operator). Angles: float32(pos * rope_scale) *
+ *   rope_theta^(-2k/head_dim) for dims k and k + head_dim/2; rotated values are
+ *   evaluated in float32 and rounded to dtype.
+ * q_rope_position may be NULL when rotary_mode == 0.
+ * tree_size = mn_indptr[batch] (rows of tree_mask); total_kv = kv_indptr[batch].
+ * Supported: head_dim 64 or 128, dtype fp16/bf16, any h_q divisible by h_kv.
+ */
+ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, const void* v,
+                       const int32_t* kv_indptr, const int32_t* q_rope_position,
+                       const int32_t* mn_indptr, const int32_t* tree_mask, void* out, float* lse,
+                       int32_t batch, int32_t total_q, int32_t total_kv, int32_t tree_size,
+                       int32_t h_q, int32_t h_kv, int32_t head_dim, ra_dtype dtype,
+                       int32_t rotary_mode, float rope_scale, float rope_theta, float sm_scale,
+                       hipStream_t stream);
+
+/*
+ * Ragged prefill or tree attention over a paged KV cache (the paged_prefill_attn
+ * operation). Page gather and lengths follow "_kernel_common.py" page,
+ * _get_kv_chunk_len / _get_seq_offset, and the paged tree kernel on the
+ * "tree_attn.py" page:
+ *   sequence b owns pages page_values[page_indptr[b] .. page_indptr[b+1]);
+ *   with np pages its KV chunk holds
+ *     kv_len = (np-1)*page_size + last_page_len                (no window)
+ *     kv_len = (np-1)*page_size + last_page_len - offset + sink (window)
+ *   (kv_len = 0 when np == 0); chunk position j lives at storage offset
+ *   o = j, or o = (j < sink ? j : j - sink + offset) with the window, i.e.
+ *   in page page_values[page_indptr[b] + o / page_size], slot o % page_size.
+ * length_info: [batch] last_page_len when sliding_window == 0, else
+ *   [3, batch] rows (last_page_len, window offset, sink size).
+ * Mask: when tree_order is given, the tree test of ra_tree_attn with the tree
+ *   being the last tree_order_indptr[b+1] - tree_order_indptr[b] chunk
+ *   columns (everything before it is a fully visible prefix); otherwise
+ *   _causal_mask: causal != 0 -> j < kv_len - qo_len + i + 1, else j < kv_len.
+ * rotary_mode: 0 = none; 1 = q row r rotated at q_rope_position[r], and K at
+ *   chunk position j rotated at k_rope_pos_offset[b] + j when
+ *   k_rope_pos_offset is non-NULL (when it is NULL, K is used as stored:
+ *   the cache's K was rotated before caching, see ra_paged_kv_append).
+ * nnz_pages = page_indptr[batch]; tree_size = tree_order_indptr[batch] (0 when
+ *   no tree). page_size must be 16. A sliding window combined with a tree
+ *   mask is RA_EUNSUPPORTED (the page's paged tree kernel disables it).
+ */
+ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* pages,
+                        const int32_t* page_indptr, const int32_t* page_values,
+                        const int32_t* length_info, int32_t sliding_window,
+                        const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
+                        const int32_t* tree_order_indptr, const int32_t* tree_order,
+                        int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
+                        int32_t num_pages, int32_t nnz_pages, int32_t tree_size,
+                        int32_t page_size, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                        ra_dtype dtype, int32_t rotary_mode, float rope_scale, float rope_theta,
+                        float sm_scale, hipStream_t stream);
+
+/*
+ * Append new K/V tokens into the paged cache, rotating K first when
+ * rope_position is non-NULL (the "normal" RoPE mode of the KV cache on the
+ * "_kernel_common.py" page, RopeMode: RoPE applied to k before adding it to
+ * the cache).
+ *
+ * k, v [n_tokens, h_kv, head_dim]; tokens [append_indptr[b], append_indptr[b+1])
+ * belong to sequence b and go to storage offsets append_start[b] + 0, 1, ...
+ * i.e. page page_values[page_indptr[b] + o / page_size], slot o % page_size,
+ * of pages [num_pages, 2, h_kv, page_size, head_dim]. K is rotated at
+ * rope_position[token] with the angles of ra_tree_attn. A token whose page
+ * index falls outside page_values or the pool is skipped.
+ */
+ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append_indptr,
+                             const int32_t* append_start, const int32_t* rope_position,
+                             const int32_t* page_indptr, const int32_t* page_values, void* pages,
+                             int32_t batch, int32_t n_tokens, int32_t num_pages,
+                             int32_t nnz_pages, int32_t page_size, int32_t h_kv,
+                             int32_t head_dim, ra_dtype dtype, float rope_scale,
+                             float rope_theta, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAGATTN_H */

@@ -1,0 +1,71 @@
+"""CPU checks of the benchmark's work accounting and of the parity tolerance.
+
+bench.visible_pairs uses closed forms (tree depth + 1 ancestors, causal row
+limits); here they are checked against the oracle's masks counted directly.
+"""
+
+import numpy as np
+import torch
+
+import bench
+import oracle
+from tests.parity import out_tolerance
+from workloads import make_config, make_custom_paged, make_custom_tree
+
+
+def _count_with_oracle(w):
+    total = 0
+    L = bench.chunk_lengths(w)
+    for b in range(w.batch):
+        q0, q1 = int(w.q_indptr[b]), int(w.q_indptr[b + 1])
+        qo = q1 - q0
+        if qo == 0:
+            continue
+        rows = np.arange(qo)
+        if w.kind == "tree":
+            vis = oracle.tree_visible(w.tree_mask[int(w.mn_indptr[b]):int(w.mn_indptr[b + 1])], rows, int(L[b]), qo)
+        elif w.tree_order is not None:
+            t = w.tree_order[int(w.tree_order_indptr[b]):int(w.tree_order_indptr[b + 1])]
+            vis = oracle.tree_visible(t, rows, int(L[b]), qo)
+        else:
+            vis = oracle.causal_visible(rows, int(L[b]), qo, w.causal)
+        total += int(vis.sum())
+    return total * w.h_q
+
+
+def test_visible_pairs_tree_and_causal():
+    cases = [
+        make_config(0),
+        make_config(1),
+        make_custom_tree(1, [0, 5, 33], h_q=4, h_kv=2, d=64, dtype="f16", max_children=2),
+        make_custom_paged(2, [7, 40, 0], [30, 40, 5], h_q=4, h_kv=1, d=64, dtype="bf16", causal=1),
+        make_custom_paged(3, [7, 40], [30, 20], h_q=4, h_kv=1, d=64, dtype="bf16", causal=0),
+        make_custom_paged(4, [20, 9], [200, 77], h_q=4, h_kv=2, d=64, dtype="bf16", causal=1,
+                          sliding=([136, 37], [4, 0])),
+        make_custom_paged(5, [6, 11], [26, 14], h_q=4, h_kv=2, d=64, dtype="f16", causal=0, tree=True),
+    ]
+    for w in cases:
+        assert bench.visible_pairs(w) == _count_with_oracle(w), w.name
+
+
+def test_sliding_config_pairs_closed_form():
+    w = make_config(3)
+    # 4 sequences, chunk 4100, 1024 causal rows: row r sees 3077 + r columns
+    assert bench.visible_pairs(w) == 4 * sum(3077 + r for r in range(1024)) * 64
+
+
+def test_algorithmic_bytes_tree_batched():
+    w = make_config(1)
+    q = 1024 * 32 * 128 * 2
+    kv = 1024 * 8 * 128 * 2 * 2
+    lse = 1024 * 32 * 4
+    idx = 4 * 17 * 2 + 4 * 17 + 8 * 1024 + 4 * 1024
+    assert bench.algorithmic_bytes(w) == 2 * q + kv + lse + idx
+
+
+def test_out_tolerance_only_relaxes_where_dtype_cannot_hold_1e2():
+    bf, hf = torch.bfloat16, torch.float16
+    assert np.all(out_tolerance(np.array([0.0, 0.3, 1.9, 3.99, -3.5]), bf) == 1e-2)
+    assert np.all(out_tolerance(np.array([0.0, 5.0, 31.0]), hf) == 1e-2)
+    assert abs(out_tolerance(np.array([5.0]), bf)[0] - (2.0 ** -6 + 2e-3)) < 1e-12
+    assert abs(out_tolerance(np.array([-9.0]), bf)[0] - (2.0 ** -5 + 2e-3)) < 1e-12

@@ -1,0 +1,138 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol that
+include/*.h declares, and rejects bad arguments with the documented status
+before launching anything (no GPU needed: validation runs on the host)."""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_ragged_gqa_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(ra_[a-z_0-9]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ra.lib_path()):
+        pytest.fail("libragattn.so is not built (run __graft_entry__.build())")
+    return ra.library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == set(ra.EXPORTED_SYMBOLS)
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ra.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ra_[a-z_0-9]+)\b", out))
+    assert _declared() <= exported
+    for name in _declared():
+        assert getattr(lib, name) is not None
+
+
+def _tree(lib, **kw):
+    a = dict(batch=1, total_q=4, total_kv=4, tree_size=4, h_q=8, h_kv=2, d=128, dtype=0, rot=0,
+             scale=1.0, theta=1e4, sm=0.1)
+    a.update(kw)
+    P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    nul = None
+    ptrs = [P] * 10
+    for i in kw.get("null", ()):
+        ptrs[i] = nul
+    return lib.ra_tree_attn(*ptrs, a["batch"], a["total_q"], a["total_kv"], a["tree_size"], a["h_q"],
+                            a["h_kv"], a["d"], a["dtype"], a["rot"], a["scale"], a["theta"], a["sm"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_q=6, h_kv=4), ra.RA_EINVAL),
+    (dict(h_kv=0), ra.RA_EINVAL),
+    (dict(batch=-1), ra.RA_EINVAL),
+    (dict(rot=2), ra.RA_EINVAL),
+    (dict(sm=0.0), ra.RA_EINVAL),
+    (dict(sm=float("nan")), ra.RA_EINVAL),
+    (dict(rot=1, theta=-1.0), ra.RA_EINVAL),
+    (dict(null=(0,)), ra.RA_EINVAL),            # q
+    (dict(null=(7,)), ra.RA_EINVAL),            # tree_mask
+    (dict(null=(4,)), ra.RA_EINVAL),            # kv_indptr
+    (dict(rot=1, null=(5,)), ra.RA_EINVAL),     # q_rope_position
+    (dict(d=96), ra.RA_EUNSUPPORTED),
+    (dict(dtype=7), ra.RA_EUNSUPPORTED),
+])
+def test_tree_attn_rejects(lib, kw, status):
+    assert _tree(lib, **kw) == status
+    assert ra.ra_last_error() != ""
+
+
+def test_empty_problem_is_ok_without_launch(lib):
+    assert _tree(lib, batch=0, total_q=0) == ra.RA_OK
+    assert ra.ra_last_error() == ""
+
+
+def _paged(lib, **kw):
+    a = dict(sliding=0, causal=1, batch=1, total_q=4, num_pages=4, nnz=4, tree_size=0, page=16,
+             h_q=8, h_kv=2, d=128, dtype=1, rot=0, scale=1.0, theta=1e4, sm=0.1)
+    a.update(kw)
+    P = ctypes.c_void_p(0x1000)
+    ptrs = {"q": P, "q_indptr": P, "pages": P, "page_indptr": P, "page_values": P, "length_info": P,
+            "k_rope_pos_offset": None, "q_rope_position": None, "tree_order_indptr": None,
+            "tree_order": None, "out": P, "lse": P}
+    ptrs.update(kw.get("ptrs", {}))
+    return lib.ra_paged_attn(ptrs["q"], ptrs["q_indptr"], ptrs["pages"], ptrs["page_indptr"],
+                             ptrs["page_values"], ptrs["length_info"], a["sliding"],
+                             ptrs["k_rope_pos_offset"], ptrs["q_rope_position"],
+                             ptrs["tree_order_indptr"], ptrs["tree_order"], a["causal"], ptrs["out"],
+                             ptrs["lse"], a["batch"], a["total_q"], a["num_pages"], a["nnz"],
+                             a["tree_size"], a["page"], a["h_q"], a["h_kv"], a["d"], a["dtype"],
+                             a["rot"], a["scale"], a["theta"], a["sm"], None)
+
+
+P_ = ctypes.c_void_p(0x1000)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=32), ra.RA_EUNSUPPORTED),
+    (dict(sliding=2), ra.RA_EINVAL),
+    (dict(sliding=1, tree_size=4, ptrs={"tree_order_indptr": P_, "tree_order": P_}), ra.RA_EUNSUPPORTED),
+    (dict(ptrs={"tree_order": P_}), ra.RA_EINVAL),                       # tree without indptr
+    (dict(tree_size=4, ptrs={"tree_order_indptr": P_}), ra.RA_EINVAL),  # indptr without tree
+    (dict(rot=1), ra.RA_EINVAL),                                          # no q_rope_position
+    (dict(ptrs={"page_indptr": None}), ra.RA_EINVAL),
+    (dict(ptrs={"length_info": None}), ra.RA_EINVAL),
+    (dict(h_q=12, h_kv=8), ra.RA_EINVAL),
+    (dict(d=256), ra.RA_EUNSUPPORTED),
+])
+def test_paged_attn_rejects(lib, kw, status):
+    assert _paged(lib, **kw) == status
+    assert ra.ra_last_error() != ""
+
+
+def test_append_rejects(lib):
+    P = ctypes.c_void_p(0x1000)
+    st = lib.ra_paged_kv_append(P, P, P, P, None, P, P, P, 0, 5, 4, 4, 16, 2, 128, 1, 1.0, 1e4, None)
+    assert st == ra.RA_EINVAL                                   # tokens without sequences
+    st = lib.ra_paged_kv_append(P, P, P, P, None, P, P, P, 1, 5, 4, 4, 8, 2, 128, 1, 1.0, 1e4, None)
+    assert st == ra.RA_EUNSUPPORTED                             # page_size 8
+    st = lib.ra_paged_kv_append(P, None, P, P, None, P, P, P, 1, 5, 4, 4, 16, 2, 128, 1, 1.0, 1e4, None)
+    assert st == ra.RA_EINVAL                                   # v NULL
+    st = lib.ra_paged_kv_append(P, P, P, P, None, P, P, P, 1, 0, 4, 4, 16, 2, 128, 1, 1.0, 1e4, None)
+    assert st == ra.RA_OK                                       # nothing to append
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("RAGATTN_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ra, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        ra.library()

@@ -1,0 +1,164 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small cases are compared element by element on every row; they span several
+128-row query tiles and 64-key KV tiles with ragged tails. The five workloads
+run at their full sizes in the same launch configuration the benchmark times,
+compared on sampled query tokens (all heads of each), plus properties checked
+on every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import DeviceInputs, compare, run_oracle, sample_rows, say
+from workloads import make_config, make_custom_paged, make_custom_tree
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_ragged_gqa_amd as ra
+    ra.library()
+
+
+def _check(w, label, rows=None):
+    say("[gpu] %s: launching (b=%d total_q=%d h=%d/%d d=%d %s)" % (label, w.batch, w.total_q, w.h_q, w.h_kv, w.d, w.dtype))
+    di = DeviceInputs(w)
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    say("[gpu] %s: done" % label)
+    ref_out, ref_lse = run_oracle(w, rows=rows)
+    d_out, d_lse = compare(out, lse, ref_out, ref_lse, rows=rows, label=label)
+    say("[gpu] %s: max|d out| %.2e  max rel|d lse| %.2e" % (label, d_out, d_lse))
+    return di
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [0, 1])
+def test_config_parity_full(k):
+    _check(make_config(k), "config%d" % k)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_config_parity_sampled(k):
+    w = make_config(k)
+    rows = sample_rows(w, per_seq=4, seed=k)
+    di = _check(w, "config%d" % k, rows=rows)
+    # properties on every row: finite, no empty rows in these workloads
+    lse = di.lse.float().cpu().numpy()
+    assert np.isfinite(lse).all()
+    assert torch.isfinite(di.out.float()).all().item()
+
+
+# ---------------------------------------------------------------------------
+# contiguous tree attention, small shapes
+# ---------------------------------------------------------------------------
+
+TREE_CASES = [
+    dict(seed=1, sizes=[1, 37, 64, 300], h_q=32, h_kv=8, d=128, dtype="f16", rotary_mode=1, max_children=4),
+    dict(seed=2, sizes=[5, 129, 250], h_q=6, h_kv=2, d=64, dtype="bf16", rotary_mode=0),
+    dict(seed=3, sizes=[200], h_q=4, h_kv=4, d=64, dtype="f16", rotary_mode=1, position_offset=5000),
+    dict(seed=4, sizes=[17, 90], h_q=16, h_kv=2, d=128, dtype="bf16", rotary_mode=1, rope_theta=5e5),
+    dict(seed=5, sizes=[0, 3, 0, 65], h_q=8, h_kv=1, d=128, dtype="f16", rotary_mode=0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TREE_CASES)))
+def test_tree_small(case):
+    c = dict(TREE_CASES[case])
+    seed, sizes = c.pop("seed"), c.pop("sizes")
+    w = make_custom_tree(seed, sizes, **c)
+    _check(w, "tree_small[%d]" % case)
+
+
+def test_tree_chain_and_singletons():
+    # a chain (causal) and a forest of singletons in one batch
+    w = make_custom_tree(6, [70, 40], h_q=8, h_kv=2, d=128, dtype="bf16")
+    w.tree_mask = np.concatenate([
+        np.stack([np.arange(70), np.full(70, 70)], axis=1),          # chain: node i ancestor of all later
+        np.stack([np.arange(40), np.arange(1, 41)], axis=1)]).astype(np.int32)
+    _check(w, "tree_chain_singletons")
+
+
+# ---------------------------------------------------------------------------
+# paged KV, small shapes
+# ---------------------------------------------------------------------------
+
+PAGED_CASES = [
+    dict(seed=11, qo=[1, 100, 257, 3], stored=[1, 400, 288, 3], h_q=32, h_kv=8, d=128, dtype="bf16", causal=1, extra_pages=7),
+    dict(seed=12, qo=[64, 33], stored=[64, 200], h_q=4, h_kv=2, d=64, dtype="f16", causal=1),
+    dict(seed=13, qo=[50, 130], stored=[20, 130], h_q=8, h_kv=1, d=128, dtype="bf16", causal=1),   # kv < qo: empty rows
+    dict(seed=14, qo=[40, 7], stored=[90, 200], h_q=64, h_kv=8, d=128, dtype="bf16", causal=0),
+    dict(seed=15, qo=[0, 5, 0, 7], stored=[10, 0, 0, 30], h_q=6, h_kv=3, d=64, dtype="f16", causal=1),
+    dict(seed=16, qo=[50, 10, 200], stored=[300, 64, 1000], h_q=64, h_kv=8, d=128, dtype="bf16", causal=1,
+         sliding=([200, 0, 800], [4, 0, 16])),
+    dict(seed=17, qo=[300], stored=[330], h_q=8, h_kv=8, d=128, dtype="bf16", causal=1,
+         sliding=([100], [0])),                                                 # qo > chunk
+    dict(seed=18, qo=[1, 40, 130], stored=[1, 117, 330], h_q=64, h_kv=8, d=128, dtype="bf16", causal=0,
+         tree=True, tree_max_children=4, tree_max_depth=16, store_rope="tree", rotary_mode=1, rope_theta=5e5),
+    dict(seed=19, qo=[20, 64], stored=[20, 96], h_q=8, h_kv=2, d=64, dtype="f16", causal=0, tree=True,
+         tree_max_children=2),
+    dict(seed=20, qo=[8, 15, 70], stored=[30, 15, 170], h_q=4, h_kv=2, d=64, dtype="f16", causal=1,
+         rotary_mode=1, k_rope_pos_offset=[5, 100, 2000]),
+    dict(seed=21, qo=[300, 44], stored=[900, 44], h_q=32, h_kv=8, d=128, dtype="bf16", causal=1,
+         store_rope="linear", rope_theta=1e4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PAGED_CASES)))
+def test_paged_small(case):
+    c = dict(PAGED_CASES[case])
+    seed, qo, stored = c.pop("seed"), c.pop("qo"), c.pop("stored")
+    w = make_custom_paged(seed, qo, stored, **c)
+    _check(w, "paged_small[%d]" % case)
+
+
+# ---------------------------------------------------------------------------
+# append (RoPE before caching), determinism, streams
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_append_matches_oracle_rope(dtype, d):
+    import attention_ragged_gqa_amd as ra
+    from tests.parity import gpu_pages
+    from workloads import pages_from_logical
+    w = make_custom_paged(30, [5, 9], [70, 300], h_q=4, h_kv=2, d=d, dtype=dtype, causal=1,
+                          store_rope="linear", rope_theta=5e5)
+    w.store_rope_position = (w.store_rope_position * 13 + 7).astype(np.int32)   # large angles
+    say("[gpu] append %s d=%d" % (dtype, d))
+    pool = gpu_pages(w, "cuda:0")
+    torch.cuda.synchronize()
+    ref = pages_from_logical(w)
+    kr = torch.from_numpy(oracle.rope(w.k_store, w.store_rope_position, 5e5, 1.0, dtype)).to(w.q.dtype)
+    w.k_store = kr
+    ref_rot = pages_from_logical(w)
+    got = pool.cpu()
+    assert torch.equal(got[:, 1], ref[:, 1])                 # V copied bit-exactly
+    gk, rk = got[:, 0].double(), ref_rot[:, 0].double()
+    diff = (gk - rk).abs()
+    ulp = rk.abs().clamp_min(2.0 ** -14) * (2.0 ** (-10 if dtype == "f16" else -7))
+    assert bool((diff <= ulp).all()), "rotated K off by more than one ulp"
+    assert (diff > 0).double().mean().item() < 5e-3, "too many rounding flips"
+
+
+def test_deterministic_and_side_stream():
+    w = make_custom_paged(31, [200, 77], [700, 77], h_q=32, h_kv=8, d=128, dtype="bf16", causal=1)
+    di = DeviceInputs(w)
+    say("[gpu] determinism")
+    out1, lse1 = di.launch()
+    out1, lse1 = out1.clone(), lse1.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        di.out.zero_()
+        out2, lse2 = di.launch(stream=s)
+    s.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)

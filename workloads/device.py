@@ -1,0 +1,81 @@
+"""Stage a workload on the GPU and launch it through the library's Python
+binding (used by the tests, the smoke test and the benchmark).
+
+Paged workloads whose K is rotated before caching get their page pool from
+the library's append kernel (ra_paged_kv_append), which rotates K on the way
+in; the others copy the generator's pages. Nothing here computes attention.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .generators import pages_from_logical
+
+
+def _i32(a, dev):
+    return None if a is None else torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
+
+
+def gpu_pages(w, dev):
+    """Page pool on the device. K rotated before caching is written by the
+    library's append kernel; otherwise the generator's pages are copied."""
+    import attention_ragged_gqa_amd as ra
+    if w.store_rope_position is None:
+        return pages_from_logical(w).to(dev)
+    pool = torch.zeros((w.num_pages, 2, w.h_kv, 16, w.d), dtype=w.q.dtype, device=dev)
+    ra.ra_paged_kv_append(w.k_store.to(dev), w.v_store.to(dev), _i32(w.kv_store_indptr, dev),
+                          torch.zeros(w.batch, dtype=torch.int32, device=dev),
+                          _i32(w.store_rope_position, dev), _i32(w.page_indptr, dev),
+                          _i32(w.page_values, dev), pool, rope_scale=w.rope_scale,
+                          rope_theta=w.rope_theta)
+    return pool
+
+
+class DeviceInputs:
+    """All device tensors of one workload, built once, so the same launch can
+    be repeated (tests, bench)."""
+
+    def __init__(self, w, dev="cuda:0"):
+        self.w = w
+        self.dev = torch.device(dev)
+        d = self.dev
+        self.q = w.q.to(d)
+        self.q_indptr = _i32(w.q_indptr, d)
+        self.q_rope_position = _i32(w.q_rope_position, d) if w.rotary_mode == 1 else None
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(w.total_q, w.h_q, dtype=torch.float32, device=d)
+        if w.kind == "tree":
+            self.k = w.k.to(d)
+            self.v = w.v.to(d)
+            self.kv_indptr = _i32(w.kv_indptr, d)
+            self.mn_indptr = _i32(w.mn_indptr, d)
+            self.tree_mask = _i32(w.tree_mask.reshape(-1, 2), d)
+        else:
+            self.pages = gpu_pages(w, d)
+            self.page_indptr = _i32(w.page_indptr, d)
+            self.page_values = _i32(w.page_values, d)
+            self.length_info = _i32(w.length_info, d)
+            self.k_rope_pos_offset = _i32(w.k_rope_pos_offset, d)
+            self.tree_order_indptr = _i32(w.tree_order_indptr, d)
+            self.tree_order = _i32(None if w.tree_order is None else w.tree_order.reshape(-1, 2), d)
+
+    def launch(self, stream=None):
+        import attention_ragged_gqa_amd as ra
+        w = self.w
+        if w.kind == "tree":
+            return ra.ra_tree_attn(self.q, self.q_indptr, self.k, self.v, self.kv_indptr,
+                                   self.q_rope_position, self.mn_indptr, self.tree_mask,
+                                   out=self.out, lse=self.lse, rotary_mode=w.rotary_mode,
+                                   rope_scale=w.rope_scale, rope_theta=w.rope_theta,
+                                   sm_scale=w.sm_scale, stream=stream)
+        return ra.ra_paged_attn(self.q, self.q_indptr, self.pages, self.page_indptr,
+                                self.page_values, self.length_info,
+                                sliding_window=w.sliding_window,
+                                k_rope_pos_offset=self.k_rope_pos_offset,
+                                q_rope_position=self.q_rope_position,
+                                tree_order_indptr=self.tree_order_indptr,
+                                tree_order=self.tree_order, causal=w.causal, out=self.out,
+                                lse=self.lse, rotary_mode=w.rotary_mode, rope_scale=w.rope_scale,
+                                rope_theta=w.rope_theta, sm_scale=w.sm_scale, stream=stream)

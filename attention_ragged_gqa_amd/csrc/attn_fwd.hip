@@ -90,8 +90,9 @@ __device__ bool locate_item(const AttnParams& p, int& b, int& kvh, int& tile) {
 template <bool BF, int D, int LAYOUT, int MASK>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int CH = D / 8;               // 16-byte chunks per head row
-  constexpr int KROWS = kThreads / CH;    // K rows staged per pass
-  constexpr int KP = kBN / KROWS;         // K passes per tile
+  constexpr int HC = CH / 2;              // chunk pairs (dims k and k + D/2)
+  constexpr int KSTEP = kThreads / HC;    // K rows staged per pass
+  constexpr int KP = kBN / KSTEP;         // K passes per tile
   constexpr int KS = D * 2 + 16;          // LDS K row stride (bytes)
   constexpr int VS = kBN * 2 + 16;        // LDS V^T row stride (bytes)
   constexpr int K_OFF = 0;
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int BUF = T_OFF + kBN * 8;
   constexpr int VUNITS = 16 * CH;         // (4-key group, chunk) pairs
   static_assert(KP >= 1 && VUNITS <= kThreads, "tile shape");
+  static_assert((kBM / 1 + 1) * (D / 2) * 8 <= 2 * BUF, "RoPE table fits in the tile buffers");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
   __shared__ double inv_freq_s[D / 2];
@@ -174,7 +176,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   }
 
   // ---- rotary frequency table ----
-  if (p.rope_q | p.rope_k) {
+  const bool any_rope = p.rope_q | p.rope_k;
+  if (any_rope) {
     if (tid < D / 2) inv_freq_s[tid] = exp2(-(2.0 * tid / D) * p.log2_theta);
     __syncthreads();
   }
@@ -187,67 +190,73 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     const uint16_t* qrow = p.q + (static_cast<size_t>(q0 + t) * p.h_q + head) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
-    if (p.rope_q) {
-      const int pos = p.q_rope_position[q0 + t];
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        u32x4 a = qf[s], c2 = qf[s + D / 32];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float y1[2], y2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float cs, sn;
-            rope_cos_sin(pos, p.rope_scale, inv_freq_s[16 * s + 8 * hh + e + u], cs, sn);
-            rope_pair(cs, sn, to_f32<BF>(half_of(a, e + u)), to_f32<BF>(half_of(c2, e + u)),
-                      y1[u], y2[u]);
-          }
-          qf[s][e >> 1] = pack2<BF>(y1[0], y1[1]);
-          qf[s + D / 32][e >> 1] = pack2<BF>(y2[0], y2[1]);
-        }
-      }
-    }
   }
 
   // ---- K/V tile staging ----
-  const int kc = tid % CH;          // K: chunk
-  const int krow = tid / CH;        // K: first row
+  const int kpc = tid % HC;          // K: chunk pair (chunks kpc and kpc + HC)
+  const int kkey = tid / HC;         // K: first row, then + KSTEP
   const bool v_active = tid < VUNITS;
-  const int vg = tid & 15;          // V: 4-key group
-  const int vc = tid >> 4;          // V: chunk
+  const int vg = tid & 15;           // V: 4-key group
+  const int vc = tid >> 4;           // V: chunk
 
-  auto kv_row = [&](int kidx, int which) -> const uint16_t* {
+  // storage offset of chunk position kidx (sliding window: sink, then window)
+  auto seq_off = [&](int kidx) -> int {
+    return (p.sliding && kidx >= sink) ? kidx - sink + win_off : kidx;
+  };
+  // page holding chunk position kidx, or -1 (paged layout only)
+  auto page_of = [&](int kidx) -> int {
+    if (kidx >= kv_len) return -1;
+    const int off = seq_off(kidx);
+    if (off < 0) return -1;
+    const int pi = page_base + (off >> 4);
+    if (pi < 0 || pi >= page_end) return -1;
+    const int page = p.page_values[pi];
+    return static_cast<unsigned>(page) < static_cast<unsigned>(p.num_pages) ? page : -1;
+  };
+  // Page numbers of this thread's K and V rows in the next tile to load,
+  // fetched one tile ahead of the K/V loads that use them.
+  int kpage[KP], vpage[4];
+  auto fetch_pages = [&](int j0) {
+    if constexpr (LAYOUT == kPaged) {
+#pragma unroll
+      for (int i = 0; i < KP; ++i) kpage[i] = page_of(j0 + kkey + i * KSTEP);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vpage[k] = v_active ? page_of(j0 + 4 * vg + k) : -1;
+    }
+  };
+  auto kv_row = [&](int kidx, int which, int page) -> const uint16_t* {
     if (kidx >= kv_len) return nullptr;
     if constexpr (LAYOUT == kContiguous) {
       const int r = kv_base + kidx;
       if (r < 0 || r >= p.total_kv) return nullptr;
       return (which ? p.v : p.k) + (static_cast<size_t>(r) * p.h_kv + kvh) * D;
     } else {
-      const int off = (p.sliding && kidx >= sink) ? kidx - sink + win_off : kidx;
-      if (off < 0) return nullptr;
-      const int pi = page_base + (off >> 4);
-      if (pi < 0 || pi >= page_end) return nullptr;
-      const int page = p.page_values[pi];
-      if (static_cast<unsigned>(page) >= static_cast<unsigned>(p.num_pages)) return nullptr;
-      return p.pages + (((static_cast<size_t>(page) * 2 + which) * p.h_kv + kvh) * 16 + (off & 15)) * D;
+      if (page < 0) return nullptr;
+      return p.pages + (((static_cast<size_t>(page) * 2 + which) * p.h_kv + kvh) * 16 + (seq_off(kidx) & 15)) * D;
     }
   };
 
-  u32x4 kreg[KP];
+  u32x4 klo[KP], khi[KP];
   u32x4 vreg[4];
   int tree_e = 0, tree_x = 0;
 
+  // global loads of one K/V tile into registers (pages from fetch_pages)
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
-      const int kidx = j0 + krow + i * KROWS;
-      const uint16_t* src = kv_row(kidx, 0);
-      kreg[i] = src ? *reinterpret_cast<const u32x4*>(src + 8 * kc) : u32x4{0, 0, 0, 0};
+      const uint16_t* src = kv_row(j0 + kkey + i * KSTEP, 0, kpage[i]);
+      if (src) {
+        klo[i] = *reinterpret_cast<const u32x4*>(src + 8 * kpc);
+        khi[i] = *reinterpret_cast<const u32x4*>(src + 8 * (kpc + HC));
+      } else {
+        klo[i] = u32x4{0, 0, 0, 0};
+        khi[i] = u32x4{0, 0, 0, 0};
+      }
     }
     if (v_active) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint16_t* src = kv_row(j0 + 4 * vg + k, 1);
+        const uint16_t* src = kv_row(j0 + 4 * vg + k, 1, vpage[k]);
         vreg[k] = src ? *reinterpret_cast<const u32x4*>(src + 8 * vc) : u32x4{0, 0, 0, 0};
       }
     }
@@ -269,42 +278,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         }
       }
     }
-    if (p.rope_k) {
-      // partner chunk (dims +- D/2) sits in lane ^ (CH/2), same row
+  };
+
+  // rotate the staged K rows in registers (this thread holds both halves)
+  auto rope_k_tile = [&](int j0) {
 #pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        u32x4 other;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) other[u] = __shfl_xor(kreg[i][u], CH / 2, 64);
-        const int kidx = j0 + krow + i * KROWS;
-        if (kidx < kv_len) {
-          int pos;
-          if constexpr (LAYOUT == kContiguous) {
-            const int pi = kv_base + kidx;   // K positions share the query position array
-            pos = (pi >= 0 && pi < p.total_q) ? p.q_rope_position[pi] : 0;
-          } else {
-            pos = p.k_rope_pos_offset[b] + kidx;
-          }
-          const bool first = kc < CH / 2;
-          u32x4 res;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float y[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int dim = 8 * kc + e + u;
-              float cs, sn;
-              rope_cos_sin(pos, p.rope_scale, inv_freq_s[dim & (D / 2 - 1)], cs, sn);
-              const float x = to_f32<BF>(half_of(kreg[i], e + u));
-              const float xp = to_f32<BF>(half_of(other, e + u));
-              float y1, y2;
-              if (first) rope_pair(cs, sn, x, xp, y1, y2), y[u] = y1;
-              else rope_pair(cs, sn, xp, x, y1, y2), y[u] = y2;
-            }
-            res[e >> 1] = pack2<BF>(y[0], y[1]);
-          }
-          kreg[i] = res;
+    for (int i = 0; i < KP; ++i) {
+      const int kidx = j0 + kkey + i * KSTEP;
+      if (kidx < kv_len) {
+        int pos;
+        if constexpr (LAYOUT == kContiguous) {
+          const int pi = kv_base + kidx;   // K positions share the query position array
+          pos = (pi >= 0 && pi < p.total_q) ? p.q_rope_position[pi] : 0;
+        } else {
+          pos = p.k_rope_pos_offset[b] + kidx;
         }
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float cs, sn;
+            rope_cos_sin(pos, p.rope_scale, inv_freq_s[8 * kpc + e + u], cs, sn);
+            rope_pair(cs, sn, to_f32<BF>(half_of(klo[i], e + u)), to_f32<BF>(half_of(khi[i], e + u)),
+                      y1[u], y2[u]);
+          }
+          lo[e >> 1] = pack2<BF>(y1[0], y1[1]);
+          hi[e >> 1] = pack2<BF>(y2[0], y2[1]);
+        }
+        klo[i] = lo;
+        khi[i] = hi;
       }
     }
   };
@@ -312,8 +316,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   auto store_tile = [&](int bufi) {
     char* buf = smem + bufi * BUF;
 #pragma unroll
-    for (int i = 0; i < KP; ++i)
-      *reinterpret_cast<u32x4*>(buf + K_OFF + (krow + i * KROWS) * KS + kc * 16) = kreg[i];
+    for (int i = 0; i < KP; ++i) {
+      char* row = buf + K_OFF + (kkey + i * KSTEP) * KS;
+      *reinterpret_cast<u32x4*>(row + kpc * 16) = klo[i];
+      *reinterpret_cast<u32x4*>(row + (kpc + HC) * 16) = khi[i];
+    }
     if (v_active) {
       // keys 4*vg..4*vg+3 -> V^T positions: within each group of 16 keys the
       // 4-key quarters are stored in the order 0, 2, 1, 3
@@ -332,8 +339,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
+  // first K/V tile in flight before the Q rotation
+  if (n_tiles > 0) {
+    fetch_pages(0);
+    load_tile(0);
+    if (n_tiles > 1) fetch_pages(kBN);
+  }
+
+  // ---- RoPE on Q: a cos/sin table per (token of this tile, frequency) in
+  // the tile buffers, shared by the g heads of each token ----
+  if (p.rope_q) {
+    const int t_first = row0 / g;
+    const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
+    const int n_entries = max(t_end - t_first, 0) * (D / 2);
+    float2* tab = reinterpret_cast<float2*>(smem);
+    for (int e = tid; e < n_entries; e += kThreads) {
+      const int tl = e / (D / 2);
+      const int kf = e - tl * (D / 2);
+      const int qi = q0 + t_first + tl;
+      const int pos = (qi >= 0 && qi < p.total_q) ? p.q_rope_position[qi] : 0;
+      float cs, sn;
+      rope_cos_sin(pos, p.rope_scale, inv_freq_s[kf], cs, sn);
+      tab[e] = make_float2(cs, sn);
+    }
+    __syncthreads();
+    if (row_ok) {
+      const float2* trow = tab + (t - t_first) * (D / 2);
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const u32x4 a = qf[s], c2 = qf[s + D / 32];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float2 cs = trow[16 * s + 8 * hh + e + u];
+            rope_pair(cs.x, cs.y, to_f32<BF>(half_of(a, e + u)), to_f32<BF>(half_of(c2, e + u)),
+                      y1[u], y2[u]);
+          }
+          qf[s][e >> 1] = pack2<BF>(y1[0], y1[1]);
+          qf[s + D / 32][e >> 1] = pack2<BF>(y2[0], y2[1]);
+        }
+      }
+    }
+    __syncthreads();   // the tile buffers are reused for K/V below
+  }
+
   // ---- online softmax state (row R; both half-waves carry it) ----
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;   // reference max (log2 domain), shared by both halves
   float l_run = 0.f;
   f32x16 o[D / 32];
 #pragma unroll
@@ -341,14 +394,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const float sc = p.sm_scale_log2;
 
   if (n_tiles > 0) {
-    load_tile(0);
+    if (p.rope_k) rope_k_tile(0);
     store_tile(0);
   }
   __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
     const int j0 = it * kBN;
-    if (it + 1 < n_tiles) load_tile(j0 + kBN);
+    if (it + 1 < n_tiles) {
+      load_tile(j0 + kBN);
+      if (it + 2 < n_tiles) fetch_pages(j0 + 2 * kBN);
+    }
     const char* buf = smem + (it & 1) * BUF;
 
     // tile class for this wave: 0 skip, 1 full, 2 partial
@@ -391,14 +447,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * sc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+      mx = pair_max(mx) * sc;
+      // The O / l rescale is skipped when no row of the wave has a new max.
+      const bool grow = mx > m_run;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -422,12 +483,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
           o[db] = mma32<BF>(*reinterpret_cast<const u32x4*>(vp + 32 * db * VS), pf, o[db]);
       }
     }
-    if (it + 1 < n_tiles) store_tile((it + 1) & 1);
+    if (it + 1 < n_tiles) {
+      if (p.rope_k) rope_k_tile(j0 + kBN);
+      store_tile((it + 1) & 1);
+    }
     __syncthreads();
   }
 
   // ---- epilogue: out = O / l (dtype), lse = m + log2(l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(q0 + t) * p.h_q + head) * D;

@@ -17,20 +17,30 @@
 //  * A workgroup is 4 waves of 64; each wave owns 32 packed rows. Scores are
 //    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}:
 //    each lane then holds one query row and 16 keys per 32-key block, so row
-//    max and row sum are in-lane plus one exchange with lane ^ 32, and the
-//    fp32 accumulators convert in place into the B operand of O^T += V^T P^T.
-//  * Q stays in registers (RoPE applied on load). K tiles are staged in LDS
-//    row-major; V tiles are transposed in registers and staged as V^T with
-//    keys permuted so each lane's 8 keys of a PV step are one 16-byte read.
-//    Global loads for tile i+1 are issued before tile i is computed (LDS is
-//    double buffered, one barrier per tile).
+//    max and row sum are in-lane plus one v_permlane32_swap, and the fp32
+//    accumulators convert in place into the B operand of O^T += V^T P^T.
+//  * Q stays in registers (RoPE applied on load, from a per-tile cos/sin
+//    table shared by the g heads of a token).
+//  * K and V tiles (64 keys) go from HBM straight into LDS with
+//    global_load_lds_dwordx4 (no staging registers), two stages deep, as
+//    row-major tiles whose 16-byte chunks are XOR-swizzled per row. The LDS
+//    serves 256 bytes (64 banks) per clock; with rr = the row's index in
+//    256-byte units, K chunk c sits at c ^ (rr mod 16 chunks) so the b128
+//    K-operand reads of 16 consecutive rows hit distinct banks, and V chunk
+//    c sits at c ^ 4(rr mod 4) so ds_read_b64_tr_b16 (which returns 4
+//    consecutive keys of one dim per lane) reads 4 rows x 32 bytes per
+//    16-lane group without conflicts (both measured). With in-kernel K RoPE
+//    the K tile is rotated in registers and written instead.
 //  * Masks are classified per (wave, tile): skipped, full (no test) or
 //    partial (per-element test); causal work stops at the last visible tile.
+//    Tree intervals of the sequence are staged in LDS once.
 //  * The softmax runs in the log2 domain (v_exp_f32 is exp2): scores are
-//    scaled by sm_scale*log2(e), lse = m + log2(l) as on the pages.
+//    scaled by sm_scale*log2(e), lse = m + log2(l) as on the pages; the O
+//    rescale is skipped when no row of the wave has a new max.
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "ra_internal.h"
@@ -39,18 +49,46 @@ namespace ra {
 
 namespace {
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int kStages = 2;
+constexpr int kTreeLds = 1024;   // tree nodes whose (enter, exit) are staged in LDS
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base wave-uniform, passed in M0). Issued through
+// inline asm so the compiler does not treat these asynchronous LDS writes as
+// aliasing every later LDS read (it would wait for them before each read and
+// undo the prefetch); wait_all_and_barrier() orders them explicitly.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const unsigned lds = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+}
+
+// Wait for this wave's outstanding global loads (including loads into LDS)
+// and LDS accesses, then the workgroup barrier. Written out because the
+// compiler neither tracks loads into LDS nor should it fence in between.
+__device__ __forceinline__ void wait_all_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Free (everything has retired), but visible to the compiler: loads it
+  // tracks need no further waits before the next DMA is issued.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+}
+
 // Locate this workgroup's work item. Returns false when the block has none.
 // Item list: for each sequence b (in order), for each KV head, ranks
 // 0..tiles_b-1 with rank 0 = the last (heaviest under a causal mask) q-tile.
-__device__ bool locate_item(const AttnParams& p, int& b, int& kvh, int& tile) {
+__device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int& b,
+                            int& kvh, int& tile) {
   const int lane = threadIdx.x & 63;
   int total = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+  for (int c0 = 0; c0 < batch; c0 += 64) {
     const int i = c0 + lane;
     int cnt = 0;
-    if (i < p.batch) {
-      const int len = max(p.q_indptr[i + 1] - p.q_indptr[i], 0);
-      cnt = ((len * p.group + kBM - 1) / kBM) * p.h_kv;
+    if (i < batch) {
+      const int len = max(q_indptr[i + 1] - q_indptr[i], 0);
+      cnt = ((len * group + kBM - 1) / kBM) * h_kv;
     }
     total += wave_sum(cnt);
   }
@@ -63,20 +101,20 @@ __device__ bool locate_item(const AttnParams& p, int& b, int& kvh, int& tile) {
   const int item = (L & 7) * chunk + slot;
   if (item >= total) return false;
   int base = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+  for (int c0 = 0; c0 < batch; c0 += 64) {
     const int i = c0 + lane;
     int cnt = 0;
-    if (i < p.batch) {
-      const int len = max(p.q_indptr[i + 1] - p.q_indptr[i], 0);
-      cnt = ((len * p.group + kBM - 1) / kBM) * p.h_kv;
+    if (i < batch) {
+      const int len = max(q_indptr[i + 1] - q_indptr[i], 0);
+      cnt = ((len * group + kBM - 1) / kBM) * h_kv;
     }
     const int incl = wave_inclusive_scan(cnt) + base;
-    const unsigned long long hit = __ballot(i < p.batch && item < incl);
+    const unsigned long long hit = __ballot(i < batch && item < incl);
     if (hit) {
       const int l = __ffsll(static_cast<long long>(hit)) - 1;
       b = c0 + l;
       const int excl = __shfl(incl - cnt, l, 64);
-      const int tiles_b = __shfl(cnt, l, 64) / p.h_kv;
+      const int tiles_b = __shfl(cnt, l, 64) / h_kv;
       const int local = item - excl;
       kvh = local / tiles_b;
       tile = tiles_b - 1 - (local - kvh * tiles_b);
@@ -87,77 +125,122 @@ __device__ bool locate_item(const AttnParams& p, int& b, int& kvh, int& tile) {
   return false;
 }
 
-template <bool BF, int D, int LAYOUT, int MASK>
+template <bool BF, int D, int LAYOUT, int MASK, bool ROPE_K>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
-  constexpr int CH = D / 8;               // 16-byte chunks per head row
-  constexpr int HC = CH / 2;              // chunk pairs (dims k and k + D/2)
-  constexpr int KSTEP = kThreads / HC;    // K rows staged per pass
-  constexpr int KP = kBN / KSTEP;         // K passes per tile
-  constexpr int KS = D * 2 + 16;          // LDS K row stride (bytes)
-  constexpr int VS = kBN * 2 + 16;        // LDS V^T row stride (bytes)
-  constexpr int K_OFF = 0;
-  constexpr int V_OFF = kBN * KS;
-  constexpr int T_OFF = V_OFF + D * VS;   // tree intervals (int2 per key)
-  constexpr int BUF = T_OFF + kBN * 8;
-  constexpr int VUNITS = 16 * CH;         // (4-key group, chunk) pairs
-  static_assert(KP >= 1 && VUNITS <= kThreads, "tile shape");
-  static_assert((kBM / 1 + 1) * (D / 2) * 8 <= 2 * BUF, "RoPE table fits in the tile buffers");
+  constexpr int RB = D * 2;                  // bytes per head row
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = kBN * RB;             // bytes of one K or V tile
+  constexpr int STAGE = 2 * TILE;            // K tile, then V tile
+  constexpr int RPL = 1024 / RB;             // rows one wave-wide 16-byte load covers
+  constexpr int LOADS = kBN / (4 * RPL);     // per wave and tile, for K and for V each
+  constexpr int TREE_OFF = kStages * STAGE;
+  constexpr int SMEM = TREE_OFF + (MASK == kMaskTree ? kTreeLds * 8 : 0);
+  static_assert(LOADS >= 1 && 4 * RPL * LOADS == kBN, "tile shape");
+  static_assert((STAGE & (STAGE - 1)) == 0, "stage size is a power of two");
+  // LDS chunk swizzles (see the header comment): K chunk c of row r sits at
+  // c ^ KSWZ(r), V chunk c at c ^ VSWZ(r); RSH = log2(rows per 256 bytes).
+  constexpr int RSH = (D == 64) ? 1 : 0;
+#define KSWZ(r) ((((r) >> RSH)) & (CH - 1))
+#define VSWZ(r) (4 * ((((r) >> RSH)) & (CH / 4 - 1)))
+  // the Q RoPE table holds at most 128 tokens x D/2 frequencies of float2
+  static_assert(128 * (D / 2) * 8 <= kStages * STAGE, "RoPE table fits in the stages");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ double inv_freq_s[D / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index as a scalar, so per-wave bounds and tile classes are uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int hh = lane >> 5;
 
-  int b = 0, kvh = 0, tile = 0;
-  if (!locate_item(p, b, kvh, tile)) return;   // uniform over the workgroup
+  // kernel arguments as scalars (nothing below takes the address of p)
+  const auto q_ = p.q;
+  const auto q_indptr_ = p.q_indptr;
+  const auto out_ = p.out;
+  const auto lse_ = p.lse;
+  const auto k_ = p.k;
+  const auto v_ = p.v;
+  const auto kv_indptr_ = p.kv_indptr;
+  const auto pages_ = p.pages;
+  const auto page_indptr_ = p.page_indptr;
+  const auto page_values_ = p.page_values;
+  const auto length_info_ = p.length_info;
+  const auto k_rope_pos_offset_ = p.k_rope_pos_offset;
+  const auto tree_indptr_ = p.tree_indptr;
+  const auto tree_order_ = p.tree_order;
+  const auto q_rope_position_ = p.q_rope_position;
+  const auto batch_ = p.batch;
+  const auto total_q_ = p.total_q;
+  const auto total_kv_ = p.total_kv;
+  const auto tree_size_ = p.tree_size;
+  const auto h_q_ = p.h_q;
+  const auto h_kv_ = p.h_kv;
+  const auto group_ = p.group;
+  const auto num_pages_ = p.num_pages;
+  const auto nnz_pages_ = p.nnz_pages;
+  const auto sliding_ = p.sliding;
+  const auto causal_ = p.causal;
+  const auto rope_q_ = p.rope_q;
+  const auto rope_k_ = p.rope_k;
+  const auto rope_scale_ = p.rope_scale;
+  const auto sm_scale_log2_ = p.sm_scale_log2;
+  const auto log2_theta_ = p.log2_theta;
 
-  const int g = p.group;
-  const int q0 = p.q_indptr[b];
-  const int qo_len = p.q_indptr[b + 1] - q0;
+  int b = 0, kvh = 0, tile = 0;
+  if (!locate_item(q_indptr_, batch_, group_, h_kv_, b, kvh, tile)) return;   // uniform over the workgroup
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  tile = __builtin_amdgcn_readfirstlane(tile);
+
+  const int g = group_;
+  const int q0 = q_indptr_[b];
+  const int qo_len = q_indptr_[b + 1] - q0;
   const int row0 = tile * kBM;
 
   // ---- KV chunk of this sequence ----
-  int kv_len = 0, kv_base = 0, page_base = 0, page_end = 0, sink = 0, win_off = 0;
+  int kv_len_m = 0, kv_base_m = 0, page_base_m = 0, page_end_m = 0, sink_m = 0, win_off_m = 0;
   if constexpr (LAYOUT == kContiguous) {
-    kv_base = p.kv_indptr[b];
-    kv_len = p.kv_indptr[b + 1] - kv_base;
+    kv_base_m = kv_indptr_[b];
+    kv_len_m = kv_indptr_[b + 1] - kv_base_m;
   } else {
-    page_base = p.page_indptr[b];
-    page_end = min(p.page_indptr[b + 1], p.nnz_pages);
-    const int np = p.page_indptr[b + 1] - page_base;
+    page_base_m = page_indptr_[b];
+    page_end_m = min(page_indptr_[b + 1], nnz_pages_);
+    const int np = page_indptr_[b + 1] - page_base_m;
     if (np > 0) {
-      if (!p.sliding) {
-        kv_len = (np - 1) * 16 + p.length_info[b];
+      if (!sliding_) {
+        kv_len_m = (np - 1) * 16 + length_info_[b];
       } else {
-        win_off = p.length_info[p.batch + b];
-        sink = p.length_info[2 * p.batch + b];
-        kv_len = (np - 1) * 16 + p.length_info[b] - win_off + sink;
+        win_off_m = length_info_[batch_ + b];
+        sink_m = length_info_[2 * batch_ + b];
+        kv_len_m = (np - 1) * 16 + length_info_[b] - win_off_m + sink_m;
       }
     }
   }
-  kv_len = max(kv_len, 0);
+  const int kv_len = max(kv_len_m, 0);
+  const int kv_base = kv_base_m, page_base = page_base_m, page_end = page_end_m;
+  const int sink = sink_m, win_off = win_off_m;
 
-  int tree_base = 0, tree_len = 0;
+  int tree_base_m = 0, tree_len_m = 0;
   if constexpr (MASK == kMaskTree) {
-    tree_base = p.tree_indptr[b];
-    tree_len = max(p.tree_indptr[b + 1] - tree_base, 0);
+    tree_base_m = tree_indptr_[b];
+    tree_len_m = max(tree_indptr_[b + 1] - tree_base_m, 0);
   }
+  const int tree_base = tree_base_m, tree_len = tree_len_m;
   const int tree_start = kv_len - tree_len;
+  const bool tree_in_lds = tree_len <= kTreeLds;   // uniform
 
   // ---- this lane's query row ----
   const int R = row0 + w * 32 + r32;
   const int t = R / g;
   const int head = kvh * g + (R - t * g);
-  const bool row_ok = t < qo_len && q0 + t >= 0 && q0 + t < p.total_q;
+  const bool row_ok = t < qo_len && q0 + t >= 0 && q0 + t < total_q_;
   const int t_lo = (row0 + w * 32) / g;
   const int t_hi = min((row0 + w * 32 + 31) / g, qo_len - 1);
   const bool wave_active = t_lo < qo_len;
 
-  const bool causal = (MASK == kMaskCausal) && p.causal;
+  const bool causal = (MASK == kMaskCausal) && causal_;
   const int lim = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
   const int lim_lo = causal ? min(kv_len, kv_len - qo_len + t_lo + 1) : kv_len;
   const int lim_hi = causal ? min(kv_len, kv_len - qo_len + t_hi + 1) : kv_len;
@@ -171,14 +254,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int enter_c = INT_MIN;   // sentinel: sees the prefix only
   if constexpr (MASK == kMaskTree) {
     const int c = t + tree_len - qo_len;
-    if (row_ok && c >= 0 && c < tree_len && tree_base + c >= 0 && tree_base + c < p.tree_size)
-      enter_c = p.tree_order[2 * (tree_base + c)];
+    if (row_ok && c >= 0 && c < tree_len && tree_base + c >= 0 && tree_base + c < tree_size_)
+      enter_c = tree_order_[2 * (tree_base + c)];
   }
 
   // ---- rotary frequency table ----
-  const bool any_rope = p.rope_q | p.rope_k;
-  if (any_rope) {
-    if (tid < D / 2) inv_freq_s[tid] = exp2(-(2.0 * tid / D) * p.log2_theta);
+  if (rope_q_ | rope_k_) {
+    if (tid < D / 2) inv_freq_s[tid] = exp2(-(2.0 * tid / D) * log2_theta_);
     __syncthreads();
   }
 
@@ -187,168 +269,155 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
   if (row_ok) {
-    const uint16_t* qrow = p.q + (static_cast<size_t>(q0 + t) * p.h_q + head) * D + 8 * hh;
+    const uint16_t* qrow = q_ + (static_cast<size_t>(q0 + t) * h_q_ + head) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
   }
 
-  // ---- K/V tile staging ----
-  const int kpc = tid % HC;          // K: chunk pair (chunks kpc and kpc + HC)
-  const int kkey = tid / HC;         // K: first row, then + KSTEP
-  const bool v_active = tid < VUNITS;
-  const int vg = tid & 15;           // V: 4-key group
-  const int vc = tid >> 4;           // V: chunk
-
-  // storage offset of chunk position kidx (sliding window: sink, then window)
-  auto seq_off = [&](int kidx) -> int {
-    return (p.sliding && kidx >= sink) ? kidx - sink + win_off : kidx;
+  // ---- K/V tile loads: wave w fills tile rows [16w, 16w + 16); lane covers
+  // rows 16w + RPL*i + lane/CH (i < LOADS) at physical chunk lane % CH ----
+  const int pc = lane % CH;
+  const int lrow = lane / CH;
+  auto tile_row = [&](int i) __attribute__((always_inline)) { return 16 * w + RPL * i + lrow; };
+  const int delta = sliding_ ? win_off - sink : 0;   // window: storage offset - position
+  // Page numbers are wave-uniform scalars: the 16 rows [B, B + 16) a wave
+  // loads (B = j0 + 16w, 16-aligned) touch at most three pages: the page of
+  // sink positions (storage offset = position) and the two pages that the
+  // window offsets starting at max(B, sink) + delta can straddle.
+  // The loaded page numbers are only inspected when the next tile is issued
+  // (after the barrier): validating them right after the load would make the
+  // compiler wait for all outstanding loads, including the K/V prefetch.
+  struct PageSet {
+    int ia, ib, ic;   // page_values indices (wave-uniform)
+    int va, vb, vc;   // raw page numbers loaded from them
+    int offb;         // first window storage offset of the block
   };
-  // page holding chunk position kidx, or -1 (paged layout only)
-  auto page_of = [&](int kidx) -> int {
-    if (kidx >= kv_len) return -1;
-    const int off = seq_off(kidx);
-    if (off < 0) return -1;
-    const int pi = page_base + (off >> 4);
-    if (pi < 0 || pi >= page_end) return -1;
-    const int page = p.page_values[pi];
-    return static_cast<unsigned>(page) < static_cast<unsigned>(p.num_pages) ? page : -1;
+  auto load_page = [&](int pidx) __attribute__((always_inline)) -> int {
+    return page_values_[min(max(pidx, 0), nnz_pages_ - 1)];   // in bounds; checked at use
   };
-  // Page numbers of this thread's K and V rows in the next tile to load,
-  // fetched one tile ahead of the K/V loads that use them.
-  int kpage[KP], vpage[4];
-  auto fetch_pages = [&](int j0) {
+  auto fetch_pages = [&](int j0) __attribute__((always_inline)) -> PageSet {
+    PageSet ps{-1, -1, -1, 0, 0, 0, 0};
     if constexpr (LAYOUT == kPaged) {
-#pragma unroll
-      for (int i = 0; i < KP; ++i) kpage[i] = page_of(j0 + kkey + i * KSTEP);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vpage[k] = v_active ? page_of(j0 + 4 * vg + k) : -1;
+      const int B = j0 + 16 * w;
+      ps.offb = (sliding_ ? max(B, sink) : B) + delta;
+      ps.ia = (sliding_ && B < sink) ? page_base + (B >> 4) : -1;
+      ps.ib = page_base + (ps.offb >> 4);
+      ps.ic = (ps.offb & 15) ? ps.ib + 1 : -1;
+      ps.va = load_page(ps.ia);
+      ps.vb = load_page(ps.ib);
+      ps.vc = load_page(ps.ic);
     }
+    return ps;
   };
-  auto kv_row = [&](int kidx, int which, int page) -> const uint16_t* {
+  auto page_ok = [&](int idx, int val) __attribute__((always_inline)) -> bool {
+    return idx >= page_base && idx < page_end &&
+           static_cast<unsigned>(val) < static_cast<unsigned>(num_pages_);
+  };
+  PageSet pages_next{-1, -1, -1, 0, 0, 0, 0};   // pages of the next tile to load
+  // byte address of the head row of chunk position kidx (K: which = 0, V: 1)
+  const size_t kv_stride = static_cast<size_t>(h_kv_) * RB;              // contiguous: per token
+  const size_t page_stride = static_cast<size_t>(2) * h_kv_ * 16 * RB;   // paged: per page
+  const char* kv_head_k;
+  const char* kv_head_v;
+  if constexpr (LAYOUT == kContiguous) {
+    kv_head_k = reinterpret_cast<const char*>(k_) + (static_cast<size_t>(kv_base) * h_kv_ + kvh) * RB;
+    kv_head_v = reinterpret_cast<const char*>(v_) + (static_cast<size_t>(kv_base) * h_kv_ + kvh) * RB;
+  } else {
+    kv_head_k = reinterpret_cast<const char*>(pages_) + static_cast<size_t>(kvh) * 16 * RB;
+    kv_head_v = kv_head_k + static_cast<size_t>(h_kv_) * 16 * RB;
+  }
+  auto row_addr = [&](int kidx, int which, PageSet ps) __attribute__((always_inline)) -> const char* {
+    const char* base = which ? kv_head_v : kv_head_k;
     if (kidx >= kv_len) return nullptr;
     if constexpr (LAYOUT == kContiguous) {
       const int r = kv_base + kidx;
-      if (r < 0 || r >= p.total_kv) return nullptr;
-      return (which ? p.v : p.k) + (static_cast<size_t>(r) * p.h_kv + kvh) * D;
+      if (r < 0 || r >= total_kv_) return nullptr;
+      return base + static_cast<size_t>(kidx) * kv_stride;
     } else {
-      if (page < 0) return nullptr;
-      return p.pages + (((static_cast<size_t>(page) * 2 + which) * p.h_kv + kvh) * 16 + (seq_off(kidx) & 15)) * D;
+      const bool in_sink = sliding_ && kidx < sink;
+      const int off = in_sink ? kidx : kidx + delta;
+      // values, not an indexed struct (which the compiler would put in memory)
+      const int ia = ps.ia, ib = ps.ib, ic = ps.ic, va = ps.va, vb = ps.vb, vc = ps.vc;
+      const bool second = (off >> 4) != (ps.offb >> 4);
+      const int idx = in_sink ? ia : (second ? ic : ib);
+      const int page = in_sink ? va : (second ? vc : vb);
+      if (!page_ok(idx, page)) return nullptr;
+      return base + static_cast<size_t>(page) * page_stride + (off & 15) * RB;
     }
   };
 
-  u32x4 klo[KP], khi[KP];
-  u32x4 vreg[4];
-  int tree_e = 0, tree_x = 0;
-
-  // global loads of one K/V tile into registers (pages from fetch_pages)
-  auto load_tile = [&](int j0) {
+  // One address and one exec region per row for both K and V.
+  const size_t v_minus_k = static_cast<size_t>(kv_head_v - kv_head_k);
+  auto issue_tile = [&](int j0, char* stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const uint16_t* src = kv_row(j0 + kkey + i * KSTEP, 0, kpage[i]);
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = tile_row(i);
+      char* dst_k = stage + (16 * w + RPL * i) * RB;          // wave-uniform
+      const char* src = row_addr(j0 + r, 0, pages_next);
       if (src) {
-        klo[i] = *reinterpret_cast<const u32x4*>(src + 8 * kpc);
-        khi[i] = *reinterpret_cast<const u32x4*>(src + 8 * (kpc + HC));
-      } else {
-        klo[i] = u32x4{0, 0, 0, 0};
-        khi[i] = u32x4{0, 0, 0, 0};
+        if constexpr (!ROPE_K)
+          dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
+        dma16(src + v_minus_k + 16 * (pc ^ VSWZ(r)), dst_k + TILE);
       }
     }
-    if (v_active) {
+  };
+
+  // In-kernel K RoPE: K goes through registers (same lanes and rows as the
+  // direct loads); the partner chunk (dims +- D/2) is in lane ^ (CH/2).
+  u32x4 kreg[ROPE_K ? LOADS : 1];
+  auto load_k_regs = [&](int j0) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint16_t* src = kv_row(j0 + 4 * vg + k, 1, vpage[k]);
-        vreg[k] = src ? *reinterpret_cast<const u32x4*>(src + 8 * vc) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = tile_row(i);
+        const char* src = row_addr(j0 + r, 0, pages_next);
+        kreg[i] = src ? *reinterpret_cast<const u32x4*>(src + 16 * (pc ^ KSWZ(r))) : u32x4{0, 0, 0, 0};
       }
     }
-    if constexpr (MASK == kMaskTree) {
-      if (tid < kBN) {
-        const int kidx = j0 + tid;
-        if (kidx >= kv_len) {
-          tree_e = INT_MAX; tree_x = INT_MIN;
-        } else if (kidx < tree_start) {
-          tree_e = INT_MIN; tree_x = INT_MAX;
-        } else {
-          const int idx = tree_base + (kidx - tree_start);
-          if (idx >= 0 && idx < p.tree_size) {
-            tree_e = p.tree_order[2 * idx];
-            tree_x = p.tree_order[2 * idx + 1];
+  };
+  auto rope_store_k = [&](int j0, char* stage) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = tile_row(i);
+        const int kidx = j0 + r;
+        const int lc = pc ^ KSWZ(r);               // logical chunk held
+        u32x4 other;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) other[u] = __shfl_xor(kreg[i][u], CH / 2, 64);
+        u32x4 res = kreg[i];
+        if (kidx < kv_len) {
+          int pos;
+          if constexpr (LAYOUT == kContiguous) {
+            const int pi = kv_base + kidx;   // K positions share the query position array
+            pos = (pi >= 0 && pi < total_q_) ? q_rope_position_[pi] : 0;
           } else {
-            tree_e = INT_MAX; tree_x = INT_MIN;
+            pos = k_rope_pos_offset_[b] + kidx;
+          }
+          const bool first = lc < CH / 2;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float cs, sn, y1, y2;
+              rope_cos_sin(pos, rope_scale_, inv_freq_s[(8 * lc + e + u) & (D / 2 - 1)], cs, sn);
+              const float x = to_f32<BF>(half_of(kreg[i], e + u));
+              const float xp = to_f32<BF>(half_of(other, e + u));
+              if (first) { rope_pair(cs, sn, x, xp, y1, y2); y[u] = y1; }
+              else { rope_pair(cs, sn, xp, x, y1, y2); y[u] = y2; }
+            }
+            res[e >> 1] = pack2<BF>(y[0], y[1]);
           }
         }
+        *reinterpret_cast<u32x4*>(stage + r * RB + 16 * pc) = res;
       }
     }
   };
-
-  // rotate the staged K rows in registers (this thread holds both halves)
-  auto rope_k_tile = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int kidx = j0 + kkey + i * KSTEP;
-      if (kidx < kv_len) {
-        int pos;
-        if constexpr (LAYOUT == kContiguous) {
-          const int pi = kv_base + kidx;   // K positions share the query position array
-          pos = (pi >= 0 && pi < p.total_q) ? p.q_rope_position[pi] : 0;
-        } else {
-          pos = p.k_rope_pos_offset[b] + kidx;
-        }
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float y1[2], y2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float cs, sn;
-            rope_cos_sin(pos, p.rope_scale, inv_freq_s[8 * kpc + e + u], cs, sn);
-            rope_pair(cs, sn, to_f32<BF>(half_of(klo[i], e + u)), to_f32<BF>(half_of(khi[i], e + u)),
-                      y1[u], y2[u]);
-          }
-          lo[e >> 1] = pack2<BF>(y1[0], y1[1]);
-          hi[e >> 1] = pack2<BF>(y2[0], y2[1]);
-        }
-        klo[i] = lo;
-        khi[i] = hi;
-      }
-    }
-  };
-
-  auto store_tile = [&](int bufi) {
-    char* buf = smem + bufi * BUF;
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      char* row = buf + K_OFF + (kkey + i * KSTEP) * KS;
-      *reinterpret_cast<u32x4*>(row + kpc * 16) = klo[i];
-      *reinterpret_cast<u32x4*>(row + (kpc + HC) * 16) = khi[i];
-    }
-    if (v_active) {
-      // keys 4*vg..4*vg+3 -> V^T positions: within each group of 16 keys the
-      // 4-key quarters are stored in the order 0, 2, 1, 3
-      const int q4 = vg & 3;
-      const int pos = 16 * (vg >> 2) + 4 * (((q4 & 1) << 1) | (q4 >> 1));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2 val;
-        val[0] = half_of(vreg[0], e) | (half_of(vreg[1], e) << 16);
-        val[1] = half_of(vreg[2], e) | (half_of(vreg[3], e) << 16);
-        *reinterpret_cast<u32x2*>(buf + V_OFF + (8 * vc + e) * VS + pos * 2) = val;
-      }
-    }
-    if constexpr (MASK == kMaskTree) {
-      if (tid < kBN) *reinterpret_cast<int2*>(buf + T_OFF + tid * 8) = make_int2(tree_e, tree_x);
-    }
-  };
-
-  // first K/V tile in flight before the Q rotation
-  if (n_tiles > 0) {
-    fetch_pages(0);
-    load_tile(0);
-    if (n_tiles > 1) fetch_pages(kBN);
-  }
 
   // ---- RoPE on Q: a cos/sin table per (token of this tile, frequency) in
-  // the tile buffers, shared by the g heads of each token ----
-  if (p.rope_q) {
+  // the stage buffers, shared by the g heads of each token ----
+  if (rope_q_) {
     const int t_first = row0 / g;
     const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
     const int n_entries = max(t_end - t_first, 0) * (D / 2);
@@ -357,9 +426,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       const int tl = e / (D / 2);
       const int kf = e - tl * (D / 2);
       const int qi = q0 + t_first + tl;
-      const int pos = (qi >= 0 && qi < p.total_q) ? p.q_rope_position[qi] : 0;
+      const int pos = (qi >= 0 && qi < total_q_) ? q_rope_position_[qi] : 0;
       float cs, sn;
-      rope_cos_sin(pos, p.rope_scale, inv_freq_s[kf], cs, sn);
+      rope_cos_sin(pos, rope_scale_, inv_freq_s[kf], cs, sn);
       tab[e] = make_float2(cs, sn);
     }
     __syncthreads();
@@ -382,31 +451,161 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         }
       }
     }
-    __syncthreads();   // the tile buffers are reused for K/V below
+    __syncthreads();   // the stage buffers are reused below
+  }
+
+  // ---- clear the stages (rows a load skips must hold finite values), stage
+  // the tree intervals ----
+  for (int off = tid * 16; off < kStages * STAGE; off += kThreads * 16)
+    *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
+  if constexpr (MASK == kMaskTree) {
+    int2* tl = reinterpret_cast<int2*>(smem + TREE_OFF);
+    const int n_st = min(tree_len, kTreeLds);
+    for (int n = tid; n < n_st; n += kThreads) {
+      const int idx = tree_base + n;
+      tl[n] = (idx >= 0 && idx < tree_size_)
+                  ? make_int2(tree_order_[2 * idx], tree_order_[2 * idx + 1])
+                  : make_int2(INT_MAX, INT_MIN);
+    }
+  }
+  __syncthreads();
+
+  // per-lane LDS byte offsets of the MFMA operands
+  int koff[D / 16];   // K rows 32*kb + r32: logical chunk 2s + hh
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) koff[s] = r32 * RB + 16 * ((2 * s + hh) ^ KSWZ(r32));
+  int voff[D / 32];   // V pieces for ds_read_b64_tr_b16 (16-lane groups)
+  {
+    const int gi = lane & 15, grp = lane >> 4;
+    const int vrow = 4 * hh + (gi >> 2);           // + 16*sp (+ 8 for the second read)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int dim = 32 * db + 16 * (grp & 1) + 4 * (gi & 3);
+      const int lc = dim >> 3;
+      voff[db] = TILE + vrow * RB + 16 * (lc ^ VSWZ(vrow)) + 2 * (dim & 7);
+    }
   }
 
   // ---- online softmax state (row R; both half-waves carry it) ----
-  float m_run = -INFINITY;   // reference max (log2 domain), shared by both halves
+  float m_run = -INFINITY;
   float l_run = 0.f;
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-  const float sc = p.sm_scale_log2;
+  const float sc = sm_scale_log2_;
 
+  // Retire every load the compiler tracks (Q rows, tree intervals) before the
+  // first LDS DMA: a wait the compiler placed for them inside the loop would
+  // also count the untracked DMAs and stall on the prefetch.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (n_tiles > 0) {
-    if (p.rope_k) rope_k_tile(0);
-    store_tile(0);
+    pages_next = fetch_pages(0);
+    issue_tile(0, smem);
+    load_k_regs(0);
+    if (n_tiles > 1) pages_next = fetch_pages(kBN);   // pages of tile 1
+    rope_store_k(0, smem);
   }
-  __syncthreads();
 
+  // One KV tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+  auto compute = [&](int j0, bool masked) __attribute__((always_inline)) {
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        sacc[kb] = mma32<BF>(*reinterpret_cast<const u32x4*>(smem + kb * 32 * RB + koff[s]), qf[s], sacc[kb]);
+    }
+    if (masked) {   // uniform: only partial tiles test each element
+      asm volatile("");   // keeps this a branch (the compiler would otherwise select)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = j0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool vis;
+          if constexpr (MASK == kMaskTree) {
+            vis = kidx < kv_len;
+            if (vis && kidx >= tree_start) {
+              const int n = kidx - tree_start;
+              int2 iv;
+              if (tree_in_lds) {
+                iv = reinterpret_cast<const int2*>(smem + TREE_OFF)[n];
+              } else {   // trees larger than the LDS copy: read the intervals directly
+                const int idx = tree_base + n;
+                iv = (idx < tree_size_) ? make_int2(tree_order_[2 * idx], tree_order_[2 * idx + 1])
+                                         : make_int2(INT_MAX, INT_MIN);
+              }
+              vis = enter_c >= iv.x && enter_c < iv.y;
+            }
+          } else {
+            vis = kidx < lim;
+          }
+          if (!vis) sacc[kb][r] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = pair_max(mx) * sc;
+    const bool grow = mx > m_run;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sc, -m_use));
+        sacc[kb][r] = pv;
+        lsum += pv;
+      }
+    l_run += lsum;
+#pragma unroll
+    for (int sp = 0; sp < kBN / 16; ++sp) {
+      const f32x16& sa = sacc[sp >> 1];
+      const int e0 = 8 * (sp & 1);
+      u32x4 pf;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pf[u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const char* vp = smem + voff[db] + 16 * sp * RB;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * RB));
+        u32x4 a;
+        a[0] = __builtin_bit_cast(u32x2, lo)[0];
+        a[1] = __builtin_bit_cast(u32x2, lo)[1];
+        a[2] = __builtin_bit_cast(u32x2, hi)[0];
+        a[3] = __builtin_bit_cast(u32x2, hi)[1];
+        o[db] = mma32<BF>(a, pf, o[db]);
+      }
+    }
+  };
+
+  // Main loop. koff / voff hold the offsets of the stage being computed and
+  // flip to the other stage (XOR STAGE, a power of two) after every tile.
+  int cur = 0;   // byte offset of the stage being computed
   for (int it = 0; it < n_tiles; ++it) {
     const int j0 = it * kBN;
+    char* next = smem + (cur ^ STAGE);
+    wait_all_and_barrier();   // tile it is in LDS; everyone is done with tile it-1
     if (it + 1 < n_tiles) {
-      load_tile(j0 + kBN);
-      if (it + 2 < n_tiles) fetch_pages(j0 + 2 * kBN);
+      issue_tile(j0 + kBN, next);
+      load_k_regs(j0 + kBN);
+      if (it + 2 < n_tiles) pages_next = fetch_pages(j0 + 2 * kBN);
     }
-    const char* buf = smem + (it & 1) * BUF;
-
     // tile class for this wave: 0 skip, 1 full, 2 partial
     int cls;
     if constexpr (MASK == kMaskTree) {
@@ -414,87 +613,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     } else {
       cls = (j0 >= lim_hi) ? 0 : ((j0 + kBN <= lim_lo) ? 1 : 2);
     }
-
-    if (wave_active && cls != 0) {
-      f32x16 sacc[2];
+    cls = __builtin_amdgcn_readfirstlane(cls);
+    if (wave_active && cls != 0) compute(j0, cls == 2);
+    if (it + 1 < n_tiles) rope_store_k(j0 + kBN, next);
+    cur ^= STAGE;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const char* kp = buf + K_OFF + (32 * kb + r32) * KS + 16 * hh;
+    for (int s = 0; s < D / 16; ++s) koff[s] ^= STAGE;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          sacc[kb] = mma32<BF>(*reinterpret_cast<const u32x4*>(kp + 32 * s), qf[s], sacc[kb]);
-      }
-      if (cls == 2) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool vis;
-            if constexpr (MASK == kMaskTree) {
-              const int2 iv = *reinterpret_cast<const int2*>(buf + T_OFF + kl * 8);
-              vis = enter_c >= iv.x && enter_c < iv.y;
-            } else {
-              vis = j0 + kl < lim;
-            }
-            if (!vis) sacc[kb][r] = -INFINITY;
-          }
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = pair_max(mx) * sc;
-      // The O / l rescale is skipped when no row of the wave has a new max.
-      const bool grow = mx > m_run;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run;
-        // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
-        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sc, -m_use));
-          sacc[kb][r] = pv;
-          lsum += pv;
-        }
-      l_run += lsum;
-#pragma unroll
-      for (int sp = 0; sp < kBN / 16; ++sp) {
-        const f32x16& sa = sacc[sp >> 1];
-        const int e0 = 8 * (sp & 1);
-        u32x4 pf;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pf[u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
-        const char* vp = buf + V_OFF + r32 * VS + 32 * sp + 16 * hh;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          o[db] = mma32<BF>(*reinterpret_cast<const u32x4*>(vp + 32 * db * VS), pf, o[db]);
-      }
-    }
-    if (it + 1 < n_tiles) {
-      if (p.rope_k) rope_k_tile(j0 + kBN);
-      store_tile((it + 1) & 1);
-    }
-    __syncthreads();
+    for (int db = 0; db < D / 32; ++db) voff[db] ^= STAGE;
   }
 
   // ---- epilogue: out = O / l (dtype), lse = m + log2(l) ----
   const float l_tot = pair_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(q0 + t) * p.h_q + head) * D;
+    uint16_t* orow = static_cast<uint16_t*>(out_) + (static_cast<size_t>(q0 + t) * h_q_ + head) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -505,23 +638,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jb + 4 * hh) = val;
       }
     if (hh == 0)
-      p.lse[static_cast<size_t>(q0 + t) * p.h_q + head] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      lse_[static_cast<size_t>(q0 + t) * h_q_ + head] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
   }
+}
+
+#undef KSWZ
+#undef VSWZ
+
+template <bool BF, int D, int LAYOUT, int MASK>
+void launch_r(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.rope_k)
+    hipLaunchKernelGGL((attn_fwd_kernel<BF, D, LAYOUT, MASK, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<BF, D, LAYOUT, MASK, false>), grid, dim3(kThreads), 0, stream, p);
 }
 
 template <bool BF, int D>
 hipError_t launch_d(const AttnParams& p, KvLayout layout, MaskKind mask, dim3 grid,
                     hipStream_t stream) {
   if (layout == kContiguous) {
-    if (mask == kMaskTree)
-      hipLaunchKernelGGL((attn_fwd_kernel<BF, D, kContiguous, kMaskTree>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<BF, D, kContiguous, kMaskCausal>), grid, dim3(kThreads), 0, stream, p);
+    if (mask == kMaskTree) launch_r<BF, D, kContiguous, kMaskTree>(p, grid, stream);
+    else launch_r<BF, D, kContiguous, kMaskCausal>(p, grid, stream);
   } else {
-    if (mask == kMaskTree)
-      hipLaunchKernelGGL((attn_fwd_kernel<BF, D, kPaged, kMaskTree>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<BF, D, kPaged, kMaskCausal>), grid, dim3(kThreads), 0, stream, p);
+    if (mask == kMaskTree) launch_r<BF, D, kPaged, kMaskTree>(p, grid, stream);
+    else launch_r<BF, D, kPaged, kMaskCausal>(p, grid, stream);
   }
   return hipGetLastError();
 }

@@ -32,9 +32,19 @@ __device__ __forceinline__ uint32_t from_f32(float x) {
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> one dword of two 16-bit values (one v_cvt_pk_{bf16,f16}_f32).
 template <bool BF>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return from_f32<BF>(lo) | (from_f32<BF>(hi) << 16);
+  const f32x2 v = {lo, hi};
+  if constexpr (BF) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
 }
 
 // Element e (0..7) of a 16-byte chunk of 16-bit values.

@@ -53,7 +53,26 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kStages = 2;
-constexpr int kTreeLds = 1024;   // tree nodes whose (enter, exit) are staged in LDS
+
+// Bounds-checked loads through a buffer resource: offsets at or past the end
+// of the range (negative offsets wrap past it) read as zero, with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = static_cast<int>(min(max(bytes, 0L), static_cast<long>(INT_MAX)));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+__device__ __forceinline__ int load_i32(__amdgpu_buffer_rsrc_t r, int index) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, 0);
+}
+__device__ __forceinline__ int2 load_i32x2(__amdgpu_buffer_rsrc_t r, int index) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, index * 8, 0, 0);
+  return make_int2(static_cast<int>(v[0]), static_cast<int>(v[1]));
+}
+// An opaque use of a loaded value at the point where it is needed: without it
+// the compiler moves dependent arithmetic up to the load and waits there,
+// before the remaining loads of the prologue have been issued.
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(double& x) { asm volatile("" : "+v"(x)); }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at lds_base + 16*l (lds_base wave-uniform, passed in M0). Issued through
@@ -79,18 +98,25 @@ __device__ __forceinline__ void wait_all_and_barrier() {
 // Locate this workgroup's work item. Returns false when the block has none.
 // Item list: for each sequence b (in order), for each KV head, ranks
 // 0..tiles_b-1 with rank 0 = the last (heaviest under a causal mask) q-tile.
+// Also returns the sequence's query offset q0 and length qo_len.
 __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int& b,
-                            int& kvh, int& tile) {
+                            int& kvh, int& tile, int& q0, int& qo_len) {
   const int lane = threadIdx.x & 63;
-  int total = 0;
-  for (int c0 = 0; c0 < batch; c0 += 64) {
-    const int i = c0 + lane;
-    int cnt = 0;
-    if (i < batch) {
-      const int len = max(q_indptr[i + 1] - q_indptr[i], 0);
-      cnt = ((len * group + kBM - 1) / kBM) * h_kv;
-    }
-    total += wave_sum(cnt);
+  // tiles * h_kv of sequence i, and its query range
+  auto count = [&](int i, int& lo, int& len) __attribute__((always_inline)) -> int {
+    lo = 0;
+    len = 0;
+    if (i >= batch) return 0;
+    lo = q_indptr[i];
+    len = max(q_indptr[i + 1] - lo, 0);
+    return ((len * group + kBM - 1) / kBM) * h_kv;
+  };
+  int lo0, len0;
+  const int cnt0 = count(lane, lo0, len0);   // first 64 sequences, kept for the search
+  int total = wave_sum(cnt0);
+  for (int c0 = 64; c0 < batch; c0 += 64) {
+    int lo, len;
+    total += wave_sum(count(c0 + lane, lo, len));
   }
   // XCD-contiguous mapping: block L runs on XCD L % 8; give XCD x the items
   // [x*chunk, (x+1)*chunk) in order.
@@ -102,19 +128,17 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
   if (item >= total) return false;
   int base = 0;
   for (int c0 = 0; c0 < batch; c0 += 64) {
-    const int i = c0 + lane;
-    int cnt = 0;
-    if (i < batch) {
-      const int len = max(q_indptr[i + 1] - q_indptr[i], 0);
-      cnt = ((len * group + kBM - 1) / kBM) * h_kv;
-    }
+    int lo = lo0, len = len0, cnt = cnt0;
+    if (c0 > 0) cnt = count(c0 + lane, lo, len);
     const int incl = wave_inclusive_scan(cnt) + base;
-    const unsigned long long hit = __ballot(i < batch && item < incl);
+    const unsigned long long hit = __ballot(c0 + lane < batch && item < incl);
     if (hit) {
       const int l = __ffsll(static_cast<long long>(hit)) - 1;
       b = c0 + l;
       const int excl = __shfl(incl - cnt, l, 64);
       const int tiles_b = __shfl(cnt, l, 64) / h_kv;
+      q0 = __shfl(lo, l, 64);
+      qo_len = __shfl(len, l, 64);
       const int local = item - excl;
       kvh = local / tiles_b;
       tile = tiles_b - 1 - (local - kvh * tiles_b);
@@ -133,8 +157,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int STAGE = 2 * TILE;            // K tile, then V tile
   constexpr int RPL = 1024 / RB;             // rows one wave-wide 16-byte load covers
   constexpr int LOADS = kBN / (4 * RPL);     // per wave and tile, for K and for V each
+  // tree masks: the (enter, exit) intervals of a tile's 64 keys, one window
+  // per stage, filled alongside the K/V tile
+  constexpr int WIN = kBN * 8;
   constexpr int TREE_OFF = kStages * STAGE;
-  constexpr int SMEM = TREE_OFF + (MASK == kMaskTree ? kTreeLds * 8 : 0);
+  constexpr int SMEM = TREE_OFF + (MASK == kMaskTree ? kStages * WIN : 0);
   static_assert(LOADS >= 1 && 4 * RPL * LOADS == kBN, "tile shape");
   static_assert((STAGE & (STAGE - 1)) == 0, "stage size is a power of two");
   // LDS chunk swizzles (see the header comment): K chunk c of row r sits at
@@ -142,8 +169,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int RSH = (D == 64) ? 1 : 0;
 #define KSWZ(r) ((((r) >> RSH)) & (CH - 1))
 #define VSWZ(r) (4 * ((((r) >> RSH)) & (CH / 4 - 1)))
-  // the Q RoPE table holds at most 128 tokens x D/2 frequencies of float2
-  static_assert(128 * (D / 2) * 8 <= kStages * STAGE, "RoPE table fits in the stages");
 
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ double inv_freq_s[D / 2];
@@ -186,50 +211,86 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const auto rope_k_ = p.rope_k;
   const auto rope_scale_ = p.rope_scale;
   const auto sm_scale_log2_ = p.sm_scale_log2;
-  const auto log2_theta_ = p.log2_theta;
 
-  int b = 0, kvh = 0, tile = 0;
-  if (!locate_item(q_indptr_, batch_, group_, h_kv_, b, kvh, tile)) return;   // uniform over the workgroup
+  // RoPE frequency of this thread (the table is written to LDS later); loaded
+  // first so that no later wait includes it
+  double ifreq = p.inv_freq[tid & 63];
+
+  int b = 0, kvh = 0, tile = 0, q0_m = 0, qo_len_m = 0;
+  if (!locate_item(q_indptr_, batch_, group_, h_kv_, b, kvh, tile, q0_m, qo_len_m))
+    return;   // uniform over the workgroup
   b = __builtin_amdgcn_readfirstlane(b);
   kvh = __builtin_amdgcn_readfirstlane(kvh);
   tile = __builtin_amdgcn_readfirstlane(tile);
+  pin(ifreq);   // arrived with the sequence table (no wait of its own later)
 
   const int g = group_;
-  const int q0 = q_indptr_[b];
-  const int qo_len = q_indptr_[b + 1] - q0;
+  const int q0 = __builtin_amdgcn_readfirstlane(q0_m);
+  const int qo_len = __builtin_amdgcn_readfirstlane(qo_len_m);
   const int row0 = tile * kBM;
 
   // ---- KV chunk of this sequence ----
+  // The per-sequence scalars come in one vector load (lane i fetches value i)
+  // and are read back with v_readlane: one round trip instead of a chain.
   int kv_len_m = 0, kv_base_m = 0, page_base_m = 0, page_end_m = 0, sink_m = 0, win_off_m = 0;
+  int li0 = 0, li1 = 0, li2 = 0, pi1 = 0, ti0 = 0, ti1 = 0, kp0 = 0;
+  {
+    const int32_t* src = q_indptr_ + b;   // any valid address for unused lanes
+    if constexpr (LAYOUT == kContiguous) {
+      if (lane == 0) src = kv_indptr_ + b;
+      if (lane == 1) src = kv_indptr_ + b + 1;
+    } else {
+      if (lane == 0) src = page_indptr_ + b;
+      if (lane == 1) src = page_indptr_ + b + 1;
+      if (lane == 2) src = length_info_ + b;
+      if (lane == 3 && sliding_) src = length_info_ + batch_ + b;
+      if (lane == 4 && sliding_) src = length_info_ + 2 * batch_ + b;
+      if (lane == 7 && ROPE_K) src = k_rope_pos_offset_ + b;
+    }
+    if constexpr (MASK == kMaskTree) {
+      if (lane == 5) src = tree_indptr_ + b;
+      if (lane == 6) src = tree_indptr_ + b + 1;
+    }
+    const int v = *src;
+    if constexpr (LAYOUT == kContiguous) {
+      kv_base_m = __builtin_amdgcn_readlane(v, 0);
+      kv_len_m = __builtin_amdgcn_readlane(v, 1);
+    } else {
+      page_base_m = __builtin_amdgcn_readlane(v, 0);
+      pi1 = __builtin_amdgcn_readlane(v, 1);
+      li0 = __builtin_amdgcn_readlane(v, 2);
+      li1 = __builtin_amdgcn_readlane(v, 3);
+      li2 = __builtin_amdgcn_readlane(v, 4);
+      kp0 = __builtin_amdgcn_readlane(v, 7);
+    }
+    if constexpr (MASK == kMaskTree) {
+      ti0 = __builtin_amdgcn_readlane(v, 5);
+      ti1 = __builtin_amdgcn_readlane(v, 6);
+    }
+  }
   if constexpr (LAYOUT == kContiguous) {
-    kv_base_m = kv_indptr_[b];
-    kv_len_m = kv_indptr_[b + 1] - kv_base_m;
+    kv_len_m -= kv_base_m;
   } else {
-    page_base_m = page_indptr_[b];
-    page_end_m = min(page_indptr_[b + 1], nnz_pages_);
-    const int np = page_indptr_[b + 1] - page_base_m;
+    page_end_m = min(pi1, nnz_pages_);
+    const int np = pi1 - page_base_m;
     if (np > 0) {
-      if (!sliding_) {
-        kv_len_m = (np - 1) * 16 + length_info_[b];
+      if (sliding_) {
+        win_off_m = li1;
+        sink_m = li2;
+        kv_len_m = (np - 1) * 16 + li0 - win_off_m + sink_m;
       } else {
-        win_off_m = length_info_[batch_ + b];
-        sink_m = length_info_[2 * batch_ + b];
-        kv_len_m = (np - 1) * 16 + length_info_[b] - win_off_m + sink_m;
+        kv_len_m = (np - 1) * 16 + li0;
       }
     }
   }
   const int kv_len = max(kv_len_m, 0);
   const int kv_base = kv_base_m, page_base = page_base_m, page_end = page_end_m;
   const int sink = sink_m, win_off = win_off_m;
-
-  int tree_base_m = 0, tree_len_m = 0;
-  if constexpr (MASK == kMaskTree) {
-    tree_base_m = tree_indptr_[b];
-    tree_len_m = max(tree_indptr_[b + 1] - tree_base_m, 0);
-  }
-  const int tree_base = tree_base_m, tree_len = tree_len_m;
+  const int tree_base = ti0, tree_len = max(ti1 - ti0, 0);
   const int tree_start = kv_len - tree_len;
-  const bool tree_in_lds = tree_len <= kTreeLds;   // uniform
+  const __amdgpu_buffer_rsrc_t pos_rsrc = make_rsrc(q_rope_position_, 4L * total_q_);
+  const __amdgpu_buffer_rsrc_t tree_rsrc = make_rsrc(tree_order_, 8L * tree_size_);
+  const int k_pos0 = kp0;   // paged: RoPE position of chunk key 0
 
   // ---- this lane's query row ----
   const int R = row0 + w * 32 + r32;
@@ -251,28 +312,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   }
   const int n_tiles = kv_hi > 0 ? (kv_hi + kBN - 1) / kBN : 0;
 
-  int enter_c = INT_MIN;   // sentinel: sees the prefix only
-  if constexpr (MASK == kMaskTree) {
-    const int c = t + tree_len - qo_len;
-    if (row_ok && c >= 0 && c < tree_len && tree_base + c >= 0 && tree_base + c < tree_size_)
-      enter_c = tree_order_[2 * (tree_base + c)];
-  }
-
-  // ---- rotary frequency table ----
-  if (rope_q_ | rope_k_) {
-    if (tid < D / 2) inv_freq_s[tid] = exp2(-(2.0 * tid / D) * log2_theta_);
-    __syncthreads();
-  }
-
-  // ---- Q fragments: lane holds row R, dims 16*s + 8*hh + [0, 8) ----
-  u32x4 qf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
-  if (row_ok) {
-    const uint16_t* qrow = q_ + (static_cast<size_t>(q0 + t) * h_q_ + head) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
-  }
+  // enter index of this row's tree node (selected after the prologue)
+  const int c_node = t + tree_len - qo_len;
+  int enter_raw = 0;
+  if constexpr (MASK == kMaskTree) enter_raw = load_i32x2(tree_rsrc, tree_base + c_node).x;
 
   // ---- K/V tile loads: wave w fills tile rows [16w, 16w + 16); lane covers
   // rows 16w + RPL*i + lane/CH (i < LOADS) at physical chunk lane % CH ----
@@ -358,6 +401,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         if constexpr (!ROPE_K)
           dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
         dma16(src + v_minus_k + 16 * (pc ^ VSWZ(r)), dst_k + TILE);
+      } else {
+        // rows past the chunk: zeros, so masked products stay finite
+        if constexpr (!ROPE_K) *reinterpret_cast<u32x4*>(dst_k + 16 * lane) = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(dst_k + TILE + 16 * lane) = u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -365,6 +412,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // In-kernel K RoPE: K goes through registers (same lanes and rows as the
   // direct loads); the partner chunk (dims +- D/2) is in lane ^ (CH/2).
   u32x4 kreg[ROPE_K ? LOADS : 1];
+  int kpos[ROPE_K ? LOADS : 1];   // RoPE positions of those rows
+  // positions first: the angles need only them and are computed while the
+  // K rows are still in flight
+  auto load_k_pos = [&](int j0) __attribute__((always_inline)) {
+    if constexpr (ROPE_K) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        if constexpr (LAYOUT == kContiguous)
+          kpos[i] = load_i32(pos_rsrc, kv_base + j0 + tile_row(i));   // K shares the query positions
+        else
+          kpos[i] = k_pos0 + j0 + tile_row(i);
+      }
+    }
+  };
   auto load_k_regs = [&](int j0) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
 #pragma unroll
@@ -375,6 +436,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       }
     }
   };
+  // The partner lanes (chunks c and c ^ CH/2 of one row) need the same 8
+  // frequencies: each evaluates 4 of them and they swap the results.
   auto rope_store_k = [&](int j0, char* stage) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
 #pragma unroll
@@ -382,30 +445,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         const int r = tile_row(i);
         const int kidx = j0 + r;
         const int lc = pc ^ KSWZ(r);               // logical chunk held
+        const bool first = lc < CH / 2;
+        int kp = kpos[i];
+        pin(kp);
+        const int pos = kidx < kv_len ? kp : 0;
+        // frequencies 8*(lc mod CH/2) + e; this lane evaluates e in [emine, emine + 4)
+        const int kbase = 8 * (lc & (CH / 2 - 1));
+        const int emine = first ? 0 : 4;
+        float cmine[4], smine[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rope_cos_sin(pos, rope_scale_, inv_freq_s[kbase + emine + u], cmine[u], smine[u]);
+        float cs[8], sn[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float co = __shfl_xor(cmine[u], CH / 2, 64);
+          const float so = __shfl_xor(smine[u], CH / 2, 64);
+          cs[u] = first ? cmine[u] : co;
+          sn[u] = first ? smine[u] : so;
+          cs[u + 4] = first ? co : cmine[u];
+          sn[u + 4] = first ? so : smine[u];
+        }
         u32x4 other;
 #pragma unroll
         for (int u = 0; u < 4; ++u) other[u] = __shfl_xor(kreg[i][u], CH / 2, 64);
         u32x4 res = kreg[i];
         if (kidx < kv_len) {
-          int pos;
-          if constexpr (LAYOUT == kContiguous) {
-            const int pi = kv_base + kidx;   // K positions share the query position array
-            pos = (pi >= 0 && pi < total_q_) ? q_rope_position_[pi] : 0;
-          } else {
-            pos = k_rope_pos_offset_[b] + kidx;
-          }
-          const bool first = lc < CH / 2;
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             float y[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              float cs, sn, y1, y2;
-              rope_cos_sin(pos, rope_scale_, inv_freq_s[(8 * lc + e + u) & (D / 2 - 1)], cs, sn);
+              float y1, y2;
               const float x = to_f32<BF>(half_of(kreg[i], e + u));
               const float xp = to_f32<BF>(half_of(other, e + u));
-              if (first) { rope_pair(cs, sn, x, xp, y1, y2); y[u] = y1; }
-              else { rope_pair(cs, sn, xp, x, y1, y2); y[u] = y2; }
+              if (first) { rope_pair(cs[e + u], sn[e + u], x, xp, y1, y2); y[u] = y1; }
+              else { rope_pair(cs[e + u], sn[e + u], xp, x, y1, y2); y[u] = y2; }
             }
             res[e >> 1] = pack2<BF>(y[0], y[1]);
           }
@@ -415,60 +489,136 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // ---- RoPE on Q: a cos/sin table per (token of this tile, frequency) in
-  // the stage buffers, shared by the g heads of each token ----
-  if (rope_q_) {
-    const int t_first = row0 / g;
-    const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
-    const int n_entries = max(t_end - t_first, 0) * (D / 2);
-    float2* tab = reinterpret_cast<float2*>(smem);
-    for (int e = tid; e < n_entries; e += kThreads) {
-      const int tl = e / (D / 2);
-      const int kf = e - tl * (D / 2);
-      const int qi = q0 + t_first + tl;
-      const int pos = (qi >= 0 && qi < total_q_) ? q_rope_position_[qi] : 0;
-      float cs, sn;
-      rope_cos_sin(pos, rope_scale_, inv_freq_s[kf], cs, sn);
-      tab[e] = make_float2(cs, sn);
+  // ---- prologue: every load that depends only on the sequence goes out
+  // together; tile 0 is in flight while RoPE tables are computed ----
+  const int t_first = row0 / g;
+  const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
+  const int n_tok = max(t_end - t_first, 0);
+  // Q RoPE table (cos, sin) per (token of this tile, frequency) in stage 1,
+  // shared by the g heads of a token; with g = 1 each lane computes its own.
+  const bool q_table = rope_q_ && n_tok * (D / 2) * 8 <= STAGE;
+  // Order of the prologue loads. Positions first (the RoPE tables need only
+  // them). Paged: the tile-0 addresses need the page numbers, so the pages
+  // go next and tile 0 is issued when they arrive, then Q. Contiguous: Q,
+  // then tile 0. (Loads complete in issue order, so whatever a wait needs
+  // should have gone out early.)
+  constexpr int TPOS = STAGE / 8 / kThreads;   // table entries per thread at most
+  static_assert(TPOS * kThreads * 8 == STAGE, "table entries per thread");
+  int tpos[TPOS];                                // token positions of those entries
+  if (q_table) {
+#pragma unroll
+    for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, q0 + t_first + (tid + u * kThreads) / (D / 2));
+  }
+  int my_pos = 0;
+  if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
+  if (n_tiles > 0) load_k_pos(0);
+  // tree intervals of tile 0 (raw: keys outside the tree part are decided
+  // by position in the mask test)
+  int2 win_iv = make_int2(0, 0);
+  if constexpr (MASK == kMaskTree) win_iv = load_i32x2(tree_rsrc, tree_base + (tid & (kBN - 1)) - tree_start);
+
+  auto issue_first_tile = [&]() __attribute__((always_inline)) {
+    if (n_tiles > 0) {
+      issue_tile(0, smem);                                 // V (and K) straight into stage 0
+      load_k_regs(0);
+      if (n_tiles > 1) pages_next = fetch_pages(kBN);      // pages of tile 1
     }
-    __syncthreads();
+  };
+  if constexpr (LAYOUT == kPaged) {
+    if (n_tiles > 0) pages_next = fetch_pages(0);
+    // one wait for the page numbers here; otherwise each row of the tile
+    // would wait again, behind the loads issued for the rows before it
+    pin(pages_next.va);
+    pin(pages_next.vb);
+    pin(pages_next.vc);
+    issue_first_tile();
+  }
+
+  // ---- Q fragments: lane holds row R, dims 16*s + 8*hh + [0, 8) ----
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
+  if (row_ok) {
+    // (token, head) row index fits in 32 bits; only the byte offset needs 64
+    const unsigned qr = static_cast<unsigned>((q0 + t) * h_q_ + head);
+    const uint16_t* qrow = q_ + static_cast<size_t>(qr) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
+  }
+  if constexpr (LAYOUT == kContiguous) issue_first_tile();
+  if (rope_q_ | rope_k_) {
+    if (tid < D / 2) inv_freq_s[tid] = ifreq;
+  }
+  __syncthreads();   // inv_freq is visible (the loads above are still in flight)
+
+  if (q_table) {
+    float2* tab = reinterpret_cast<float2*>(smem + STAGE);
+#pragma unroll
+    for (int u = 0; u < TPOS; ++u) pin(tpos[u]);
+#pragma unroll
+    for (int u = 0; u < TPOS; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < n_tok * (D / 2)) {
+        float cs, sn;
+        rope_cos_sin(tpos[u], rope_scale_, inv_freq_s[e % (D / 2)], cs, sn);
+        // 8-entry chunks of a token's row rotated by the token index, so
+        // that lanes reading different tokens' chunks hit different banks
+        const int te = e / (D / 2), kk = e % (D / 2);
+        tab[te * (D / 2) + 8 * (((kk >> 3) + te) & (D / 16 - 1)) + (kk & 7)] = make_float2(cs, sn);
+      }
+    }
+  }
+  if constexpr (MASK == kMaskTree) {
+    pin(win_iv.x);
+    pin(win_iv.y);
+    if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF)[tid] = win_iv;
+  }
+  int enter_c = INT_MIN;   // sentinel: sees the prefix only
+  if constexpr (MASK == kMaskTree) {
+    pin(enter_raw);
+    if (row_ok && c_node >= 0 && c_node < tree_len) enter_c = enter_raw;
+  }
+  if (n_tiles > 0) rope_store_k(0, smem);
+  if (rope_q_) {
+    if (q_table) __syncthreads();
+    pin(my_pos);
     if (row_ok) {
-      const float2* trow = tab + (t - t_first) * (D / 2);
+      const int tr = t - t_first;
+      const float4* trow = reinterpret_cast<const float4*>(smem + STAGE) + tr * (D / 4);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const u32x4 a = qf[s], c2 = qf[s + D / 32];
+        // frequencies 16s + 8hh + [0, 8): one 8-entry chunk of the table row
+        float cs[8], sn[8];
+        if (q_table) {
+          const float4* tc = trow + 4 * (((2 * s + hh) + tr) & (D / 16 - 1));
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float4 x = tc[v];
+            cs[2 * v] = x.x;
+            sn[2 * v] = x.y;
+            cs[2 * v + 1] = x.z;
+            sn[2 * v + 1] = x.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            rope_cos_sin(my_pos, rope_scale_, inv_freq_s[16 * s + 8 * hh + e], cs[e], sn[e]);
+        }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           float y1[2], y2[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float2 cs = trow[16 * s + 8 * hh + e + u];
-            rope_pair(cs.x, cs.y, to_f32<BF>(half_of(a, e + u)), to_f32<BF>(half_of(c2, e + u)),
+          for (int u = 0; u < 2; ++u)
+            rope_pair(cs[e + u], sn[e + u], to_f32<BF>(half_of(a, e + u)), to_f32<BF>(half_of(c2, e + u)),
                       y1[u], y2[u]);
-          }
           qf[s][e >> 1] = pack2<BF>(y1[0], y1[1]);
           qf[s + D / 32][e >> 1] = pack2<BF>(y2[0], y2[1]);
         }
       }
     }
-    __syncthreads();   // the stage buffers are reused below
   }
-
-  // ---- clear the stages (rows a load skips must hold finite values), stage
-  // the tree intervals ----
-  for (int off = tid * 16; off < kStages * STAGE; off += kThreads * 16)
-    *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
-  if constexpr (MASK == kMaskTree) {
-    int2* tl = reinterpret_cast<int2*>(smem + TREE_OFF);
-    const int n_st = min(tree_len, kTreeLds);
-    for (int n = tid; n < n_st; n += kThreads) {
-      const int idx = tree_base + n;
-      tl[n] = (idx >= 0 && idx < tree_size_)
-                  ? make_int2(tree_order_[2 * idx], tree_order_[2 * idx + 1])
-                  : make_int2(INT_MAX, INT_MIN);
-    }
-  }
-  __syncthreads();
+  // (the loop's first barrier publishes the K rows, tree intervals and tile 0)
 
   // per-lane LDS byte offsets of the MFMA operands
   int koff[D / 16];   // K rows 32*kb + r32: logical chunk 2s + hh
@@ -494,20 +644,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   const float sc = sm_scale_log2_;
 
-  // Retire every load the compiler tracks (Q rows, tree intervals) before the
-  // first LDS DMA: a wait the compiler placed for them inside the loop would
-  // also count the untracked DMAs and stall on the prefetch.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  if (n_tiles > 0) {
-    pages_next = fetch_pages(0);
-    issue_tile(0, smem);
-    load_k_regs(0);
-    if (n_tiles > 1) pages_next = fetch_pages(kBN);   // pages of tile 1
-    rope_store_k(0, smem);
-  }
-
+  int twin = TREE_OFF;   // tree window of the stage being computed
   // One KV tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
   auto compute = [&](int j0, bool masked) __attribute__((always_inline)) {
+    // visibility of the 32 elements first (bit 16kb + r: element r of block
+    // kb, key j0 + 32kb + 8(r/4) + 4hh + r%4), so that it overlaps the MFMAs
+    unsigned vbits = ~0u;
+    if (masked) {   // uniform: only partial tiles test each element
+      asm volatile("");   // keeps this a branch (the compiler would otherwise select)
+      vbits = 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kq = j0 + 32 * kb + 8 * q4 + 4 * hh;   // 4 consecutive keys
+          if constexpr (MASK == kMaskTree) {
+            const u32x4* wp = reinterpret_cast<const u32x4*>(smem + twin + 8 * (kq - j0));
+            const u32x4 a = wp[0], c = wp[1];
+            const int ex[4] = {static_cast<int>(a[0]), static_cast<int>(a[2]), static_cast<int>(c[0]),
+                               static_cast<int>(c[2])};
+            const int xx[4] = {static_cast<int>(a[1]), static_cast<int>(a[3]), static_cast<int>(c[1]),
+                               static_cast<int>(c[3])};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int kidx = kq + u;
+              const bool vis = (kidx < kv_len) &
+                               ((kidx < tree_start) | ((enter_c >= ex[u]) & (enter_c < xx[u])));
+              vbits |= static_cast<unsigned>(vis) << (16 * kb + 4 * q4 + u);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              vbits |= static_cast<unsigned>(kq + u < lim) << (16 * kb + 4 * q4 + u);
+          }
+        }
+      }
+    }
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -516,34 +688,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       for (int s = 0; s < D / 16; ++s)
         sacc[kb] = mma32<BF>(*reinterpret_cast<const u32x4*>(smem + kb * 32 * RB + koff[s]), qf[s], sacc[kb]);
     }
-    if (masked) {   // uniform: only partial tiles test each element
-      asm volatile("");   // keeps this a branch (the compiler would otherwise select)
+    if (masked) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = j0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          bool vis;
-          if constexpr (MASK == kMaskTree) {
-            vis = kidx < kv_len;
-            if (vis && kidx >= tree_start) {
-              const int n = kidx - tree_start;
-              int2 iv;
-              if (tree_in_lds) {
-                iv = reinterpret_cast<const int2*>(smem + TREE_OFF)[n];
-              } else {   // trees larger than the LDS copy: read the intervals directly
-                const int idx = tree_base + n;
-                iv = (idx < tree_size_) ? make_int2(tree_order_[2 * idx], tree_order_[2 * idx + 1])
-                                         : make_int2(INT_MAX, INT_MIN);
-              }
-              vis = enter_c >= iv.x && enter_c < iv.y;
-            }
-          } else {
-            vis = kidx < lim;
-          }
-          if (!vis) sacc[kb][r] = -INFINITY;
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          if (!((vbits >> (16 * kb + r)) & 1u)) sacc[kb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -603,7 +753,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     wait_all_and_barrier();   // tile it is in LDS; everyone is done with tile it-1
     if (it + 1 < n_tiles) {
       issue_tile(j0 + kBN, next);
+      load_k_pos(j0 + kBN);
       load_k_regs(j0 + kBN);
+      if constexpr (MASK == kMaskTree)
+        win_iv = load_i32x2(tree_rsrc, tree_base + j0 + kBN + (tid & (kBN - 1)) - tree_start);
       if (it + 2 < n_tiles) pages_next = fetch_pages(j0 + 2 * kBN);
     }
     // tile class for this wave: 0 skip, 1 full, 2 partial
@@ -615,8 +768,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
     cls = __builtin_amdgcn_readfirstlane(cls);
     if (wave_active && cls != 0) compute(j0, cls == 2);
-    if (it + 1 < n_tiles) rope_store_k(j0 + kBN, next);
+    if (it + 1 < n_tiles) {
+      rope_store_k(j0 + kBN, next);
+      if constexpr (MASK == kMaskTree)
+        if (tid < kBN) reinterpret_cast<int2*>(smem + (twin ^ WIN))[tid] = win_iv;
+    }
     cur ^= STAGE;
+    twin ^= WIN;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) koff[s] ^= STAGE;
 #pragma unroll
@@ -624,21 +782,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   }
 
   // ---- epilogue: out = O / l (dtype), lse = m + log2(l) ----
+  // O^T fragments go through LDS so that each row is stored as whole 16-byte
+  // chunks by consecutive lanes. The stage at `cur` is free: its last reads
+  // finished before the previous barrier and no load targets it.
   const float l_tot = pair_sum(l_run);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = static_cast<uint16_t*>(out_) + (static_cast<size_t>(q0 + t) * h_q_ + head) * D;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  char* obuf = smem + cur + (32 * w) * RB;   // this wave's 32 rows, same swizzle as K
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        u32x2 val;
-        val[0] = pack2<BF>(o[db][4 * jb + 0] * inv, o[db][4 * jb + 1] * inv);
-        val[1] = pack2<BF>(o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jb + 4 * hh) = val;
-      }
-    if (hh == 0)
-      lse_[static_cast<size_t>(q0 + t) * h_q_ + head] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+    for (int jb = 0; jb < 4; ++jb) {
+      // dims 32db + 8jb + 4hh + [0, 4): half hh of logical chunk 4db + jb
+      u32x2 val;
+      val[0] = pack2<BF>(o[db][4 * jb + 0] * inv, o[db][4 * jb + 1] * inv);
+      val[1] = pack2<BF>(o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
+      *reinterpret_cast<u32x2*>(obuf + r32 * RB + 16 * ((4 * db + jb) ^ KSWZ(r32)) + 8 * hh) = val;
+    }
+  if (row_ok && hh == 0)
+    lse_[static_cast<size_t>(static_cast<unsigned>((q0 + t) * h_q_ + head))] =
+        l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  // lane: chunk pc of rows lrow + RPL*i (i < 32 / RPL) of the wave's block
+#pragma unroll
+  for (int i = 0; i < 32 / RPL; ++i) {
+    const int rr = RPL * i + lrow;                 // row within the wave's 32
+    const int Rg = row0 + 32 * w + rr;
+    const int tg = Rg / g;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(obuf + rr * RB + 16 * (pc ^ KSWZ(rr)));
+    if (tg < qo_len && q0 + tg < total_q_) {
+      const unsigned orr = static_cast<unsigned>((q0 + tg) * h_q_ + kvh * g + (Rg - tg * g));
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out_) + static_cast<size_t>(orr) * D + 8 * pc) = val;
+    }
   }
 }
 

@@ -48,6 +48,15 @@ ra_status check_rope(int32_t rotary_mode, float rope_scale, float rope_theta) {
   return RA_OK;
 }
 
+// RoPE frequencies theta^(-2k/head_dim), k < head_dim / 2, in float64 (the
+// rotate-half convention of the "_kernel_common.py" page, _rope).
+void fill_inv_freq(double* inv_freq, bool rope, float theta, int32_t head_dim) {
+  for (int k = 0; k < 64; ++k)
+    inv_freq[k] = (rope && 2 * k < head_dim)
+                      ? std::pow(static_cast<double>(theta), -2.0 * k / static_cast<double>(head_dim))
+                      : 0.0;
+}
+
 ra_status launched(hipError_t e) {
   if (e != hipSuccess) return fail(RA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -103,7 +112,7 @@ ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, co
   p.rope_q = rotary_mode == 1;
   p.rope_k = rotary_mode == 1;
   p.rope_scale = rope_scale;
-  p.log2_theta = rotary_mode == 1 ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  fill_inv_freq(p.inv_freq, rotary_mode == 1, rope_theta, head_dim);
   p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kContiguous, ra::kMaskTree, stream));
 }
@@ -163,7 +172,7 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
   p.rope_q = rotary_mode == 1;
   p.rope_k = rotary_mode == 1 && k_rope_pos_offset != nullptr;
   p.rope_scale = rope_scale;
-  p.log2_theta = rotary_mode == 1 ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  fill_inv_freq(p.inv_freq, rotary_mode == 1, rope_theta, head_dim);
   p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
   return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kPaged,
                                   tree ? ra::kMaskTree : ra::kMaskCausal, stream));
@@ -205,7 +214,7 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
   p.nnz_pages = nnz_pages;
   p.h_kv = h_kv;
   p.rope_scale = rope_scale;
-  p.log2_theta = rope_position ? std::log2(static_cast<double>(rope_theta)) : 0.0;
+  fill_inv_freq(p.inv_freq, rope_position != nullptr, rope_theta, head_dim);
   return launched(ra::launch_append(p, dtype == RA_BF16, head_dim, stream));
 }
 

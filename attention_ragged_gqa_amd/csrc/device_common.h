@@ -102,11 +102,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 // k + D/2 the angle is float32(pos * scale) * inv_freq[k] with
 // inv_freq[k] = theta^(-2k/D). cos and sin are evaluated in float64 and
 // rounded once to float32, so they are the correctly rounded float32 values
-// except within ~1e-16 of a rounding boundary:
+// except within ~1e-13 (relative) of a rounding boundary:
 //   angle = pos_f * inv_freq (float64), n = nearest integer to angle/(pi/2),
 //   r = angle - n*pi/2 with pi/2 split in two parts (|r| <= pi/4 + tiny),
-//   sin r, cos r from their Taylor series through r^17 / r^16 (truncation
-//   below 1e-17 on |r| <= pi/4), then the quadrant n mod 4 picks the signs.
+//   sin r through r^15 and cos r through r^14 from their Taylor series
+//   (relative truncation below 2e-15 on |r| <= pi/4), rounded to float32,
+//   then the quadrant n mod 4 swaps and negates them.
+// n is taken as an int32, which holds it while |angle| < 3e9 (any int32
+// position with scale <= 1).
 // The rotated value is evaluated in float32 as cos*x + sin*partner (two
 // rounded products and a rounded sum, no fused multiply-add) and rounded to
 // the storage type.
@@ -121,29 +124,27 @@ __device__ __forceinline__ void rope_cos_sin(int pos, float scale, double inv_fr
   r = fma(-n, kPio2Lo, r);
   const double r2 = r * r;
   // sin r = r - r^3/3! + r^5/5! - ... ; cos r = 1 - r^2/2! + r^4/4! - ...
-  double sp = 2.8114572543455206e-15;               //  1/17!
-  sp = fma(sp, r2, -7.647163731819816e-13);         // -1/15!
+  double sp = -7.647163731819816e-13;               // -1/15!
   sp = fma(sp, r2, 1.6059043836821613e-10);         //  1/13!
   sp = fma(sp, r2, -2.505210838544172e-08);         // -1/11!
   sp = fma(sp, r2, 2.7557319223985893e-06);         //  1/9!
   sp = fma(sp, r2, -1.984126984126984e-04);         // -1/7!
   sp = fma(sp, r2, 8.333333333333333e-03);          //  1/5!
   sp = fma(sp, r2, -1.6666666666666666e-01);        // -1/3!
-  const double sr = fma(sp * r2, r, r);
-  double cp = 4.779477332387385e-14;                //  1/16!
-  cp = fma(cp, r2, -1.1470745597729725e-11);        // -1/14!
+  const float sr = static_cast<float>(fma(sp * r2, r, r));
+  double cp = -1.1470745597729725e-11;              // -1/14!
   cp = fma(cp, r2, 2.08767569878681e-09);           //  1/12!
   cp = fma(cp, r2, -2.755731922398589e-07);         // -1/10!
   cp = fma(cp, r2, 2.48015873015873e-05);           //  1/8!
   cp = fma(cp, r2, -1.388888888888889e-03);         // -1/6!
   cp = fma(cp, r2, 4.1666666666666664e-02);         //  1/4!
   cp = fma(cp, r2, -0.5);                           // -1/2!
-  const double cr = fma(cp, r2, 1.0);
-  const int q = static_cast<int>(static_cast<long long>(n) & 3);
-  const double sv = (q & 1) ? cr : sr;
-  const double cv = (q & 1) ? sr : cr;
-  s = static_cast<float>((q & 2) ? -sv : sv);
-  c = static_cast<float>(((q + 1) & 2) ? -cv : cv);
+  const float cr = static_cast<float>(fma(cp, r2, 1.0));
+  const int q = static_cast<int>(n) & 3;
+  const float sv = (q & 1) ? cr : sr;
+  const float cv = (q & 1) ? sr : cr;
+  s = (q & 2) ? -sv : sv;
+  c = ((q + 1) & 2) ? -cv : cv;
 }
 
 // y1 = cos*x1 - sin*x2 (first half), y2 = cos*x2 + sin*x1 (second half).

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int tok = blockIdx.x;
   const int tid = threadIdx.x;
   if (p.rope_position != nullptr) {
-    if (tid < D / 2) inv_freq_s[tid] = exp2(-(2.0 * tid / D) * p.log2_theta);
+    if (tid < D / 2) inv_freq_s[tid] = p.inv_freq[tid];
     __syncthreads();
   }
   // sequence of this token: last b with append_indptr[b] <= tok

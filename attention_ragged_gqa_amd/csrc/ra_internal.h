@@ -41,7 +41,7 @@ struct AttnParams {
   int32_t rope_q, rope_k;  // 0/1
   float rope_scale;
   float sm_scale_log2;     // sm_scale * log2(e)
-  double log2_theta;
+  double inv_freq[64];     // RoPE: theta^(-2k/head_dim), k < head_dim / 2
 };
 
 struct AppendParams {
@@ -55,7 +55,7 @@ struct AppendParams {
   uint16_t* pages;
   int32_t batch, n_tokens, num_pages, nnz_pages, h_kv;
   float rope_scale;
-  double log2_theta;
+  double inv_freq[64];     // RoPE: theta^(-2k/head_dim), k < head_dim / 2
 };
 
 // Launchers (attn_fwd.hip / kv_append.hip). Return the hipError_t of the launch.

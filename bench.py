@@ -14,8 +14,13 @@ line for that workload.
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
 tokens/s and the fractions of the MFMA (2.5 PFLOP/s fp16/bf16 dense) and HBM
-(8 TB/s) peaks. The kernel duration comes from HIP events recorded on the
-stream the kernel is launched on. ``roofline.traffic`` is the HBM traffic per
+(8 TB/s) peaks. The K timed steps are launched as replays of a HIP graph
+that holds --graph-launches launches (the launch path is the same C ABI call;
+the graph only removes the per-call host cost, which for small workloads is
+comparable to the kernel itself); the duration per step comes from HIP events
+recorded around the replays on the stream the kernels run on. The same
+number of eager launches is timed first and reported as
+timing.eager_ms_per_step. ``roofline.traffic`` is the HBM traffic per
 launch measured by rocprofv3 counters (profiles/<kernel>_<workload>_pmc.md),
 reported only while the kernel source is unchanged since that measurement.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the workload.
@@ -224,6 +229,10 @@ def main():
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--graph-launches", type=int, default=100,
+                    help="kernel launches captured per HIP graph (0: time eager launches)")
+    ap.add_argument("--eager-steps", type=int, default=None,
+                    help="eager launches timed for the host-issue comparison (default: --steps)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,17 +264,55 @@ def main():
     stream = torch.cuda.current_stream()       # the stream the kernel is launched on
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+
+    # Eager launches, one Python call each: for small workloads the host
+    # issue rate (ctypes + hipLaunchKernel) can be the bound, so this is
+    # reported alongside and the steps are timed as HIP graph replays.
+    eager_steps = args.steps if args.eager_steps is None else args.eager_steps
+    ms_eager = None
+    if eager_steps > 0:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(eager_steps):
+            di.launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_eager = ev0.elapsed_time(ev1) / eager_steps
+
+    use_graph = args.graph_launches > 0
+    per_graph = max(1, min(args.steps, args.graph_launches)) if use_graph else 0
+    reps, rem = divmod(args.steps, per_graph) if use_graph else (0, 0)
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                di.launch()
+        return g
+
+    if use_graph:
+        g_main = capture(per_graph)
+        g_rem = capture(rem) if rem else None
+        g_main.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        di.launch()
+    if use_graph:
+        for _ in range(reps):
+            g_main.replay()
+        if g_rem is not None:
+            g_rem.replay()
+    else:   # eager launches only (--graph-launches 0)
+        for _ in range(args.steps):
+            di.launch()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
-    log("[bench] %d steps: %.3f ms (events), %.3f s wall" % (args.steps, ms_total, wall))
+    log("[bench] %d steps as graph replays (%d launches per graph): %.3f ms (events), %.3f s wall;"
+        " eager %s ms/step" % (args.steps, per_graph, ms_total, wall,
+                               "%.5f" % ms_eager if ms_eager is not None else "-"))
 
     pairs = visible_pairs(w)
     flops = 4.0 * w.d * pairs
@@ -297,6 +344,8 @@ def main():
         "config": config_summary(w), "tokens_per_s": round(tokens_s, 1),
         "fractions": {"mfma": round(mfma_frac, 4), "hbm": round(hbm_frac, 4)},
         "unmasked_pairs": pairs, "roofline": roof,
+        "timing": {"mode": "hip_graph_replay" if use_graph else "eager", "launches_per_graph": per_graph,
+                   "eager_ms_per_step": round(ms_eager, 6) if ms_eager is not None else None},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

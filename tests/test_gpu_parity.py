@@ -162,3 +162,27 @@ def test_deterministic_and_side_stream():
         out2, lse2 = di.launch(stream=s)
     s.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_graph_replay_matches_eager():
+    """The benchmark times HIP-graph replays of the launch: every replay, with
+    eager work and synchronizations in between, must give the eager result."""
+    for w in (make_config(1),
+              make_custom_paged(32, [130, 9], [300, 40], h_q=16, h_kv=4, d=64, dtype="f16", causal=1)):
+        di = DeviceInputs(w)
+        say("[gpu] graph replay: %s" % w.name)
+        out_e, lse_e = di.launch()
+        out_e, lse_e = out_e.clone(), lse_e.clone()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            di.launch()
+        for rep in range(4):
+            di.out.fill_(7.0)
+            di.lse.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(di.out, out_e) and torch.equal(di.lse, lse_e), "replay %d differs" % rep
+            di.launch()          # eager work between replays
+            torch.cuda.synchronize()

@@ -85,6 +85,14 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
 }
 
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (the saddr form: no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16s(const char* sbase, uint32_t voff, const void* lds_base) {
+  const unsigned lds = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // Wait for this wave's outstanding global loads (including loads into LDS)
 // and LDS accesses, then the workgroup barrier. Written out because the
 // compiler neither tracks loads into LDS nor should it fence in between.
@@ -389,22 +397,101 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // One address and one exec region per row for both K and V.
+  // Tile-invariant part of each lane's source address: row RPL*i + lrow of
+  // the wave's 16-row block (one token apart when contiguous, one page slot
+  // apart when paged) and the lane's swizzled chunk. Per tile only the
+  // wave-uniform base (SGPRs) changes.
+  const uint32_t mem_rs = LAYOUT == kContiguous ? static_cast<uint32_t>(kv_stride) : RB;
+  auto lane_off = [&](int i, bool v) __attribute__((always_inline)) -> uint32_t {
+    const int r = tile_row(i);
+    return static_cast<uint32_t>(RPL * i + lrow) * mem_rs + 16 * (pc ^ (v ? VSWZ(r) : KSWZ(r)));
+  };
   const size_t v_minus_k = static_cast<size_t>(kv_head_v - kv_head_k);
+  auto zero_row = [&](char* dst) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(dst + 16 * lane) = u32x4{0, 0, 0, 0};
+  };
+  // The wave's 16-row block [B, B + 16) of tile j0 as at most two runs of
+  // rows with a common base: rows rl < split use base_a, the others base_b
+  // (paged: the block's storage offsets straddle two pages; contiguous:
+  // split = 16). Rows rl >= nvalid, or in a page that fails validation, are
+  // zero-filled. Returns false for blocks that need per-row addressing
+  // (sink positions of a sliding window).
+  struct Block {
+    const char* base_a;
+    const char* base_b;
+    int split, nvalid;
+    bool ok_a, ok_b;
+  };
+  auto block_of = [&](int j0, PageSet ps, Block& bl) __attribute__((always_inline)) -> bool {
+    const int B = j0 + 16 * w;
+    if constexpr (LAYOUT == kContiguous) {
+      bl.base_a = kv_head_k + static_cast<size_t>(B) * kv_stride;
+      bl.base_b = bl.base_a;
+      bl.split = 16;
+      bl.nvalid = min(kv_len, total_kv_ - kv_base) - B;
+      bl.ok_a = bl.ok_b = true;
+      return true;
+    } else {
+      if (sliding_ && B < sink) return false;
+      const int O = B + delta;                      // storage offset of row 0
+      const int intra = O & 15;
+      const int ia = ps.ib, ib = ps.ic;             // page_values indices
+      const int pa = __builtin_amdgcn_readfirstlane(ps.vb);
+      const int pb = __builtin_amdgcn_readfirstlane(ps.vc);
+      bl.ok_a = page_ok(ia, pa);
+      bl.ok_b = intra == 0 || page_ok(ib, pb);
+      bl.base_a = kv_head_k + static_cast<size_t>(bl.ok_a ? pa : 0) * page_stride + intra * RB;
+      bl.base_b = kv_head_k + static_cast<size_t>(bl.ok_b ? pb : 0) * page_stride - (16 - intra) * RB;
+      bl.split = 16 - intra;
+      bl.nvalid = kv_len - B;
+      return true;
+    }
+  };
+
   auto issue_tile = [&](int j0, char* stage) __attribute__((always_inline)) {
+    Block bl;
+    if (block_of(j0, pages_next, bl)) {
+      const bool whole = bl.nvalid >= 16 && bl.ok_a && bl.split == 16;   // uniform
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = tile_row(i);
-      char* dst_k = stage + (16 * w + RPL * i) * RB;          // wave-uniform
-      const char* src = row_addr(j0 + r, 0, pages_next);
-      if (src) {
-        if constexpr (!ROPE_K)
-          dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
-        dma16(src + v_minus_k + 16 * (pc ^ VSWZ(r)), dst_k + TILE);
-      } else {
-        // rows past the chunk: zeros, so masked products stay finite
-        if constexpr (!ROPE_K) *reinterpret_cast<u32x4*>(dst_k + 16 * lane) = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(dst_k + TILE + 16 * lane) = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < LOADS; ++i) {
+        char* dst_k = stage + (16 * w + RPL * i) * RB;          // wave-uniform
+        const uint32_t ok_ = lane_off(i, false), ov = lane_off(i, true);
+        if (whole) {
+          if constexpr (!ROPE_K) dma16s(bl.base_a, ok_, dst_k);
+          dma16s(bl.base_a + v_minus_k, ov, dst_k + TILE);
+        } else {
+          const int rl = RPL * i + lrow;
+          const bool in_a = rl < bl.split;
+          const bool valid = rl < bl.nvalid && (in_a ? bl.ok_a : bl.ok_b);
+          if (valid && in_a) {
+            if constexpr (!ROPE_K) dma16s(bl.base_a, ok_, dst_k);
+            dma16s(bl.base_a + v_minus_k, ov, dst_k + TILE);
+          }
+          if (valid && !in_a) {
+            if constexpr (!ROPE_K) dma16s(bl.base_b, ok_, dst_k);
+            dma16s(bl.base_b + v_minus_k, ov, dst_k + TILE);
+          }
+          if (!valid) {
+            // rows past the chunk: zeros, so masked products stay finite
+            if constexpr (!ROPE_K) zero_row(dst_k);
+            zero_row(dst_k + TILE);
+          }
+        }
+      }
+    } else {
+      // per-row addressing (blocks holding sink positions)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = tile_row(i);
+        char* dst_k = stage + (16 * w + RPL * i) * RB;
+        const char* src = row_addr(j0 + r, 0, pages_next);
+        if (src) {
+          if constexpr (!ROPE_K) dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
+          dma16(src + v_minus_k + 16 * (pc ^ VSWZ(r)), dst_k + TILE);
+        } else {
+          if constexpr (!ROPE_K) zero_row(dst_k);
+          zero_row(dst_k + TILE);
+        }
       }
     }
   };
@@ -428,11 +515,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   };
   auto load_k_regs = [&](int j0) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
+      Block bl;
+      if (block_of(j0, pages_next, bl)) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = tile_row(i);
-        const char* src = row_addr(j0 + r, 0, pages_next);
-        kreg[i] = src ? *reinterpret_cast<const u32x4*>(src + 16 * (pc ^ KSWZ(r))) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < LOADS; ++i) {
+          const int rl = RPL * i + lrow;
+          const bool in_a = rl < bl.split;
+          const bool valid = rl < bl.nvalid && (in_a ? bl.ok_a : bl.ok_b);
+          const char* base = in_a ? bl.base_a : bl.base_b;
+          kreg[i] = valid ? *reinterpret_cast<const u32x4*>(base + lane_off(i, false)) : u32x4{0, 0, 0, 0};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int r = tile_row(i);
+          const char* src = row_addr(j0 + r, 0, pages_next);
+          kreg[i] = src ? *reinterpret_cast<const u32x4*>(src + 16 * (pc ^ KSWZ(r))) : u32x4{0, 0, 0, 0};
+        }
       }
     }
   };
@@ -647,10 +746,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int twin = TREE_OFF;   // tree window of the stage being computed
   // One KV tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
   auto compute = [&](int j0, bool masked) __attribute__((always_inline)) {
-    // visibility of the 32 elements first (bit 16kb + r: element r of block
-    // kb, key j0 + 32kb + 8(r/4) + 4hh + r%4), so that it overlaps the MFMAs
+    // Tree masks: visibility of the 32 elements first (bit 16kb + r: element
+    // r of block kb, key j0 + 32kb + 8(r/4) + 4hh + r%4), so that the test
+    // overlaps the MFMAs. Causal bounds are one compare per element after.
     unsigned vbits = ~0u;
-    if (masked) {   // uniform: only partial tiles test each element
+    if (MASK == kMaskTree && masked) {   // uniform: only partial tiles test each element
       asm volatile("");   // keeps this a branch (the compiler would otherwise select)
       vbits = 0u;
 #pragma unroll
@@ -672,10 +772,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
                                ((kidx < tree_start) | ((enter_c >= ex[u]) & (enter_c < xx[u])));
               vbits |= static_cast<unsigned>(vis) << (16 * kb + 4 * q4 + u);
             }
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              vbits |= static_cast<unsigned>(kq + u < lim) << (16 * kb + 4 * q4 + u);
           }
         }
       }
@@ -689,11 +785,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         sacc[kb] = mma32<BF>(*reinterpret_cast<const u32x4*>(smem + kb * 32 * RB + koff[s]), qf[s], sacc[kb]);
     }
     if (masked) {
+      if constexpr (MASK == kMaskTree) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((vbits >> (16 * kb + r)) & 1u)) sacc[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (!((vbits >> (16 * kb + r)) & 1u)) sacc[kb][r] = -INFINITY;
+      } else {
+        // key j0 + 4hh + c(kb, r) is visible iff c < lim - j0 - 4hh
+        const int rel = lim - j0 - 4 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) sacc[kb][r] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll

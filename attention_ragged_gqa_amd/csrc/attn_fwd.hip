@@ -53,6 +53,10 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kStages = 2;
+// The O rescale is skipped while a row's running maximum grows by at most
+// this much (log2 units): probabilities then stay below 2^8, and the output
+// is normalised by the sum of the same rounded P that fed the PV MFMAs.
+constexpr float kRescaleSlack = 8.0f;
 
 // Bounds-checked loads through a buffer resource: offsets at or past the end
 // of the range (negative offsets wrap past it) read as zero, with no branch.
@@ -737,7 +741,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 
   // ---- online softmax state (row R; both half-waves carry it) ----
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;    // sum of p (float32): the log-sum-exp
+  float l_mma = 0.f;    // sum of p as rounded for the PV MFMA: the normaliser of O
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
@@ -807,13 +812,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = pair_max(mx) * sc;
-    const bool grow = mx > m_run;
+    const bool grow = mx > m_run + kRescaleSlack;   // always true while m_run = -inf
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
       // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
       m_run = m_new;
       l_run *= alpha;
+      l_mma *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
     }
@@ -834,7 +840,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       const int e0 = 8 * (sp & 1);
       u32x4 pf;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pf[u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
+      for (int u = 0; u < 4; ++u) {
+        pf[u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
+        l_mma = add_pair<BF>(pf[u], l_mma);
+      }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const char* vp = smem + voff[db] + 16 * sp * RB;
@@ -892,7 +901,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // chunks by consecutive lanes. The stage at `cur` is free: its last reads
   // finished before the previous barrier and no load targets it.
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float l_o = pair_sum(l_mma);
+  const float inv = l_o > 0.f ? 1.f / l_o : 0.f;
   char* obuf = smem + cur + (32 * w) * RB;   // this wave's 32 rows, same swizzle as K
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -904,9 +914,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       val[1] = pack2<BF>(o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
       *reinterpret_cast<u32x2*>(obuf + r32 * RB + 16 * ((4 * db + jb) ^ KSWZ(r32)) + 8 * hh) = val;
     }
-  if (row_ok && hh == 0)
-    lse_[static_cast<size_t>(static_cast<unsigned>((q0 + t) * h_q_ + head))] =
-        l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  if (row_ok && hh == 0) {
+    // the row's (token, head) index, recomputed here rather than kept live
+    // across the loop
+    int re = row0 + 32 * w + r32;
+    pin(re);
+    const int te = re / g;
+    const unsigned li = static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
+    lse_[li] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  }
   // lane: chunk pc of rows lrow + RPL*i (i < 32 / RPL) of the wave's block
 #pragma unroll
   for (int i = 0; i < 32 / RPL; ++i) {

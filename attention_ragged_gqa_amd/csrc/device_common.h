@@ -47,6 +47,20 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// c + lo + hi of a dword holding two 16-bit values (v_dot2c_f32_{f16,bf16}
+// with the constant pair (1, 1)): sums exactly the rounded values that feed
+// an MFMA.
+template <bool BF>
+__device__ __forceinline__ float add_pair(uint32_t packed, float c) {
+  if constexpr (BF) {
+    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, c, false);
+  } else {
+    const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, c, false);
+  }
+}
+
 // Element e (0..7) of a 16-byte chunk of 16-bit values.
 __device__ __forceinline__ uint32_t half_of(const u32x4& x, int e) {
   return (x[e >> 1] >> ((e & 1) * 16)) & 0xffffu;

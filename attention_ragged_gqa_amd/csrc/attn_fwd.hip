@@ -11,9 +11,10 @@
 //  * Work item = (sequence, KV head, tile of 128 packed query rows). Packed
 //    row R of a sequence is token R / g, query head kvh*g + R % g (g = h_q/h_kv),
 //    so one K/V tile feeds all g heads that share it. Items are enumerated
-//    sequence-major with the heaviest tile of each (sequence, KV head) first,
-//    and split into 8 contiguous chunks, one per XCD (workgroups are handed
-//    to XCDs round-robin), so the tiles that share K/V run on one XCD's L2.
+//    KV-head-major, then by sequence, with the heaviest tile of each
+//    (sequence, KV head) first, and split into 8 contiguous chunks, one per
+//    XCD (workgroups are handed to XCDs round-robin): the tiles that share
+//    K/V run on one XCD's L2 and every XCD gets the same mix of sequences.
 //  * A workgroup is 4 waves of 64; each wave owns 32 packed rows. Scores are
 //    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}:
 //    each lane then holds one query row and 16 keys per 32-key block, so row
@@ -108,28 +109,33 @@ __device__ __forceinline__ void wait_all_and_barrier() {
 }
 
 // Locate this workgroup's work item. Returns false when the block has none.
-// Item list: for each sequence b (in order), for each KV head, ranks
+// Item list: for each KV head, for each sequence b (in order), ranks
 // 0..tiles_b-1 with rank 0 = the last (heaviest under a causal mask) q-tile.
+// KV-head-major order: with the list cut into 8 equal chunks (one per XCD),
+// every XCD gets the same mix of long and short sequences (exactly one KV
+// head each when h_kv = 8), while all tiles of one (sequence, KV head) still
+// share an XCD's L2.
 // Also returns the sequence's query offset q0 and length qo_len.
 __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int& b,
                             int& kvh, int& tile, int& q0, int& qo_len) {
   const int lane = threadIdx.x & 63;
-  // tiles * h_kv of sequence i, and its query range
+  // q-tiles of sequence i, and its query range
   auto count = [&](int i, int& lo, int& len) __attribute__((always_inline)) -> int {
     lo = 0;
     len = 0;
     if (i >= batch) return 0;
     lo = q_indptr[i];
     len = max(q_indptr[i + 1] - lo, 0);
-    return ((len * group + kBM - 1) / kBM) * h_kv;
+    return (len * group + kBM - 1) / kBM;
   };
   int lo0, len0;
   const int cnt0 = count(lane, lo0, len0);   // first 64 sequences, kept for the search
-  int total = wave_sum(cnt0);
+  int per_head = wave_sum(cnt0);
   for (int c0 = 64; c0 < batch; c0 += 64) {
     int lo, len;
-    total += wave_sum(count(c0 + lane, lo, len));
+    per_head += wave_sum(count(c0 + lane, lo, len));
   }
+  const int total = per_head * h_kv;
   // XCD-contiguous mapping: block L runs on XCD L % 8; give XCD x the items
   // [x*chunk, (x+1)*chunk) in order.
   const int chunk = (total + 7) / 8;
@@ -138,22 +144,22 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
   if (slot >= chunk) return false;
   const int item = (L & 7) * chunk + slot;
   if (item >= total) return false;
+  kvh = item / per_head;
+  const int rem = item - kvh * per_head;
   int base = 0;
   for (int c0 = 0; c0 < batch; c0 += 64) {
     int lo = lo0, len = len0, cnt = cnt0;
     if (c0 > 0) cnt = count(c0 + lane, lo, len);
     const int incl = wave_inclusive_scan(cnt) + base;
-    const unsigned long long hit = __ballot(c0 + lane < batch && item < incl);
+    const unsigned long long hit = __ballot(c0 + lane < batch && rem < incl);
     if (hit) {
       const int l = __ffsll(static_cast<long long>(hit)) - 1;
       b = c0 + l;
       const int excl = __shfl(incl - cnt, l, 64);
-      const int tiles_b = __shfl(cnt, l, 64) / h_kv;
+      const int tiles_b = __shfl(cnt, l, 64);
       q0 = __shfl(lo, l, 64);
       qo_len = __shfl(len, l, 64);
-      const int local = item - excl;
-      kvh = local / tiles_b;
-      tile = tiles_b - 1 - (local - kvh * tiles_b);
+      tile = tiles_b - 1 - (rem - excl);
       return true;
     }
     base = __shfl(incl, 63, 64);

@@ -25,6 +25,9 @@ __all__ = [
     "EXPORTED_SYMBOLS",
     "ra_tree_attn",
     "ra_paged_attn",
+    "ra_paged_attn_split",
+    "ra_paged_attn_split_workspace",
+    "ra_merge_states",
     "ra_paged_kv_append",
     "ra_last_error",
 ]
@@ -32,7 +35,9 @@ __all__ = [
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libragattn.so"
 
-EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_paged_kv_append", "ra_last_error")
+EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_paged_attn_split",
+                    "ra_paged_attn_split_workspace", "ra_merge_states", "ra_paged_kv_append",
+                    "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
 RA_F16, RA_BF16 = 0, 1
@@ -69,6 +74,13 @@ def library() -> ctypes.CDLL:
     lib.ra_paged_attn.restype = i32
     lib.ra_paged_attn.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
                                   + [i32, i32, f32, f32, f32, vp])
+    lib.ra_paged_attn_split.restype = i32
+    lib.ra_paged_attn_split.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
+                                        + [i32, i32, f32, f32, f32, i32, vp, ctypes.c_size_t, vp])
+    lib.ra_paged_attn_split_workspace.restype = ctypes.c_size_t
+    lib.ra_paged_attn_split_workspace.argtypes = [i32] * 4
+    lib.ra_merge_states.restype = i32
+    lib.ra_merge_states.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.ra_paged_kv_append.restype = i32
     lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
     lib.ra_last_error.restype = ctypes.c_char_p
@@ -192,6 +204,79 @@ def ra_paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info,
         q_indptr.numel() - 1, total_q, num_pages, page_values.numel(), tree_size, page_size,
         h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
         _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_paged_attn_split_workspace(total_q: int, h_q: int, head_dim: int, num_kv_splits: int) -> int:
+    """Workspace bytes ra_paged_attn_split needs (C: ra_paged_attn_split_workspace)."""
+    return int(library().ra_paged_attn_split_workspace(total_q, h_q, head_dim, num_kv_splits))
+
+
+def ra_paged_attn_split(q, q_indptr, pages, page_indptr, page_values, length_info,
+                        sliding_window: int = 0, k_rope_pos_offset=None, q_rope_position=None,
+                        tree_order_indptr=None, tree_order=None, causal: int = 1, out=None,
+                        lse=None, rotary_mode: int = 0, rope_scale: float = 1.0,
+                        rope_theta: float = 1e4, sm_scale: Optional[float] = None,
+                        num_kv_splits: int = 0, workspace=None, stream=None):
+    """Split-KV paged attention (C: ra_paged_attn_split). Arguments as
+    ra_paged_attn, plus num_kv_splits (0: the library chooses) and an optional
+    uint8 device workspace; when it is None one is allocated here for the
+    largest split count (64). Returns (out, lse)."""
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    _check_dev("pages", pages, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("page_indptr", page_indptr),
+                    ("page_values", page_values), ("length_info", length_info),
+                    ("k_rope_pos_offset", k_rope_pos_offset), ("q_rope_position", q_rope_position),
+                    ("tree_order_indptr", tree_order_indptr), ("tree_order", tree_order)):
+        _check_dev(name, t, i32, dev)
+    if pages.dim() != 5 or pages.shape[1] != 2:
+        raise ValueError("pages must be [num_pages, 2, h_kv, page_size, d]")
+    out, lse = _out_lse(q, out, lse)
+    total_q, h_q, d = q.shape
+    num_pages, _, h_kv, page_size, dp = pages.shape
+    if dp != d:
+        raise ValueError("pages head_dim %d != q head_dim %d" % (dp, d))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        n = ra_paged_attn_split_workspace(total_q, h_q, d, num_kv_splits if num_kv_splits > 0 else 64)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _check_dev("workspace", workspace, None, dev)
+    tree_size = 0 if tree_order is None else tree_order.shape[0]
+    st = library().ra_paged_attn_split(
+        _ptr(q), _ptr(q_indptr), _ptr(pages), _ptr(page_indptr), _ptr(page_values),
+        _ptr(length_info), int(sliding_window), _ptr(k_rope_pos_offset), _ptr(q_rope_position),
+        _ptr(tree_order_indptr), _ptr(tree_order), int(causal), _ptr(out), _ptr(lse),
+        q_indptr.numel() - 1, total_q, num_pages, page_values.numel(), tree_size, page_size,
+        h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
+        int(num_kv_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_merge_states(part_out, part_lse, out, lse, stream=None):
+    """Merge split-KV partial states (C: ra_merge_states).
+
+    part_out [S, rows, d] fp32, part_lse [S, rows] fp32 (base-2 lse);
+    out [rows, d] (or [tokens, heads, d]) fp16/bf16, lse [rows] fp32."""
+    dev = part_out.device
+    _check_dev("part_out", part_out, torch.float32, dev)
+    _check_dev("part_lse", part_lse, torch.float32, dev)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be fp16 or bf16")
+    _check_dev("out", out, None, dev)
+    _check_dev("lse", lse, torch.float32, dev)
+    S, rows, d = part_out.shape
+    if tuple(part_lse.shape) != (S, rows) or out.numel() != rows * d or lse.numel() != rows:
+        raise ValueError("shapes: part_out [S, rows, d], part_lse [S, rows], out rows*d, lse rows")
+    st = library().ra_merge_states(_ptr(part_out), _ptr(part_lse), S, rows, d, _DTYPES[out.dtype],
+                                   _ptr(out), _ptr(lse), _stream(dev, stream))
     _raise(st)
     return out, lse
 

@@ -115,9 +115,10 @@ __device__ __forceinline__ void wait_all_and_barrier() {
 // every XCD gets the same mix of long and short sequences (exactly one KV
 // head each when h_kv = 8), while all tiles of one (sequence, KV head) still
 // share an XCD's L2.
+// With split-KV (splits > 1) each q-tile is `splits` items, one per KV range.
 // Also returns the sequence's query offset q0 and length qo_len.
-__device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int& b,
-                            int& kvh, int& tile, int& q0, int& qo_len) {
+__device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int splits,
+                            int& b, int& kvh, int& tile, int& split, int& q0, int& qo_len) {
   const int lane = threadIdx.x & 63;
   // q-tiles of sequence i, and its query range
   auto count = [&](int i, int& lo, int& len) __attribute__((always_inline)) -> int {
@@ -126,7 +127,7 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
     if (i >= batch) return 0;
     lo = q_indptr[i];
     len = max(q_indptr[i + 1] - lo, 0);
-    return (len * group + kBM - 1) / kBM;
+    return (len * group + kBM - 1) / kBM * splits;
   };
   int lo0, len0;
   const int cnt0 = count(lane, lo0, len0);   // first 64 sequences, kept for the search
@@ -156,10 +157,13 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
       const int l = __ffsll(static_cast<long long>(hit)) - 1;
       b = c0 + l;
       const int excl = __shfl(incl - cnt, l, 64);
-      const int tiles_b = __shfl(cnt, l, 64);
+      const int tiles_b = __shfl(cnt, l, 64) / splits;
       q0 = __shfl(lo, l, 64);
       qo_len = __shfl(len, l, 64);
-      tile = tiles_b - 1 - (rem - excl);
+      const int local = rem - excl;
+      const int rank = local / splits;
+      split = local - rank * splits;
+      tile = tiles_b - 1 - rank;
       return true;
     }
     base = __shfl(incl, 63, 64);
@@ -234,12 +238,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // first so that no later wait includes it
   double ifreq = p.inv_freq[tid & 63];
 
-  int b = 0, kvh = 0, tile = 0, q0_m = 0, qo_len_m = 0;
-  if (!locate_item(q_indptr_, batch_, group_, h_kv_, b, kvh, tile, q0_m, qo_len_m))
+  const int splits = max(p.num_splits, 1);
+  int b = 0, kvh = 0, tile = 0, split_m = 0, q0_m = 0, qo_len_m = 0;
+  if (!locate_item(q_indptr_, batch_, group_, h_kv_, splits, b, kvh, tile, split_m, q0_m, qo_len_m))
     return;   // uniform over the workgroup
   b = __builtin_amdgcn_readfirstlane(b);
   kvh = __builtin_amdgcn_readfirstlane(kvh);
   tile = __builtin_amdgcn_readfirstlane(tile);
+  const int split = __builtin_amdgcn_readfirstlane(split_m);
   pin(ifreq);   // arrived with the sequence table (no wait of its own later)
 
   const int g = group_;
@@ -328,7 +334,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     const int t_last = min((row0 + kBM - 1) / g, qo_len - 1);
     kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
   }
-  const int n_tiles = kv_hi > 0 ? (kv_hi + kBN - 1) / kBN : 0;
+  const int n_tiles_all = kv_hi > 0 ? (kv_hi + kBN - 1) / kBN : 0;
+  // split-KV: this item's contiguous range of those tiles
+  const int tile_lo = (splits > 1) ? split * n_tiles_all / splits : 0;
+  const int tile_hi = (splits > 1) ? (split + 1) * n_tiles_all / splits : n_tiles_all;
+  const int n_tiles = tile_hi - tile_lo;   // tiles this workgroup processes
+  const int jbase = tile_lo * kBN;         // first key of the range
 
   // enter index of this row's tree node (selected after the prologue)
   const int c_node = t + tree_len - qo_len;
@@ -620,21 +631,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   }
   int my_pos = 0;
   if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
-  if (n_tiles > 0) load_k_pos(0);
+  if (n_tiles > 0) load_k_pos(jbase);
   // tree intervals of tile 0 (raw: keys outside the tree part are decided
   // by position in the mask test)
   int2 win_iv = make_int2(0, 0);
-  if constexpr (MASK == kMaskTree) win_iv = load_i32x2(tree_rsrc, tree_base + (tid & (kBN - 1)) - tree_start);
+  if constexpr (MASK == kMaskTree)
+    win_iv = load_i32x2(tree_rsrc, tree_base + jbase + (tid & (kBN - 1)) - tree_start);
 
   auto issue_first_tile = [&]() __attribute__((always_inline)) {
     if (n_tiles > 0) {
-      issue_tile(0, smem);                                 // V (and K) straight into stage 0
-      load_k_regs(0);
-      if (n_tiles > 1) pages_next = fetch_pages(kBN);      // pages of tile 1
+      issue_tile(jbase, smem);                             // V (and K) straight into stage 0
+      load_k_regs(jbase);
+      if (n_tiles > 1) pages_next = fetch_pages(jbase + kBN);   // pages of the second tile
     }
   };
   if constexpr (LAYOUT == kPaged) {
-    if (n_tiles > 0) pages_next = fetch_pages(0);
+    if (n_tiles > 0) pages_next = fetch_pages(jbase);
     // one wait for the page numbers here; otherwise each row of the tile
     // would wait again, behind the loads issued for the rows before it
     pin(pages_next.va);
@@ -687,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     pin(enter_raw);
     if (row_ok && c_node >= 0 && c_node < tree_len) enter_c = enter_raw;
   }
-  if (n_tiles > 0) rope_store_k(0, smem);
+  if (n_tiles > 0) rope_store_k(jbase, smem);
   if (rope_q_) {
     if (q_table) __syncthreads();
     pin(my_pos);
@@ -869,7 +881,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // flip to the other stage (XOR STAGE, a power of two) after every tile.
   int cur = 0;   // byte offset of the stage being computed
   for (int it = 0; it < n_tiles; ++it) {
-    const int j0 = it * kBN;
+    const int j0 = jbase + it * kBN;
     char* next = smem + (cur ^ STAGE);
     wait_all_and_barrier();   // tile it is in LDS; everyone is done with tile it-1
     if (it + 1 < n_tiles) {
@@ -909,6 +921,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const float l_tot = pair_sum(l_run);
   const float l_o = pair_sum(l_mma);
   const float inv = l_o > 0.f ? 1.f / l_o : 0.f;
+  if (splits > 1) {
+    // split-KV partial state: O / l in fp32 and the range's lse, row-major at
+    // [split][row]; the merge kernel combines the ranges
+    if (row_ok) {
+      int re = row0 + 32 * w + r32;
+      pin(re);
+      const int te = re / g;
+      const size_t li = static_cast<size_t>(split) * total_q_ * h_q_ +
+                        static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
+      float* prow = p.part_out + li * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const float4 v = make_float4(o[db][4 * jb + 0] * inv, o[db][4 * jb + 1] * inv,
+                                       o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
+          *reinterpret_cast<float4*>(prow + 32 * db + 8 * jb + 4 * hh) = v;
+        }
+      if (hh == 0) p.part_lse[li] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+    }
+    return;
+  }
   char* obuf = smem + cur + (32 * w) * RB;   // this wave's 32 rows, same swizzle as K
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -974,7 +1008,7 @@ hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout 
   // Upper bound on the number of work items, plus slack so that the
   // XCD-contiguous mapping (8 * ceil(items / 8) blocks) always fits.
   const long tiles = (static_cast<long>(p.total_q) * p.group + kBM - 1) / kBM + p.batch;
-  long blocks = tiles * p.h_kv + 7;
+  long blocks = tiles * p.h_kv * (p.num_splits > 1 ? p.num_splits : 1) + 7;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks > INT_MAX) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));

@@ -2,6 +2,7 @@
 // Nothing here touches device memory; every call launches at most one kernel
 // on the caller's stream and returns without synchronising.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -117,7 +118,39 @@ ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, co
   return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kContiguous, ra::kMaskTree, stream));
 }
 
-ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* pages,
+}  // extern "C"
+
+namespace {
+
+// ---- split-KV ------------------------------------------------------------
+constexpr int32_t kMaxSplits = 64;
+
+size_t part_out_bytes(size_t rows, int32_t head_dim, int32_t splits) {
+  const size_t b = static_cast<size_t>(splits) * rows * head_dim * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+size_t split_workspace_bytes(int32_t total_q, int32_t h_q, int32_t head_dim, int32_t splits) {
+  if (splits <= 1 || total_q <= 0 || h_q <= 0) return 0;
+  const size_t rows = static_cast<size_t>(total_q) * h_q;
+  return part_out_bytes(rows, head_dim, splits) + static_cast<size_t>(splits) * rows * sizeof(float);
+}
+
+// Splits so that about four workgroups per CU (1024) have work, with at
+// least two 64-key tiles per split on the average sequence (KV lengths are
+// on the device; the page count gives their mean).
+int32_t auto_splits(int32_t batch, int32_t total_q, int32_t group, int32_t h_kv, int32_t nnz_pages) {
+  const long items = std::max<long>((static_cast<long>(total_q) * group + ra::kBM - 1) / ra::kBM,
+                                    batch) * h_kv;
+  const long tiles = static_cast<long>(nnz_pages) * 16 / std::max(batch, 1) / ra::kBN;
+  long s = (1024 + items - 1) / std::max(items, 1L);
+  s = std::min(s, tiles / 2);
+  return static_cast<int32_t>(std::max(1L, std::min<long>(s, kMaxSplits)));
+}
+
+}  // namespace
+
+static ra_status paged_attn_impl(const void* q, const int32_t* q_indptr, const void* pages,
                         const int32_t* page_indptr, const int32_t* page_values,
                         const int32_t* length_info, int32_t sliding_window,
                         const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
@@ -126,7 +159,8 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
                         int32_t num_pages, int32_t nnz_pages, int32_t tree_size,
                         int32_t page_size, int32_t h_q, int32_t h_kv, int32_t head_dim,
                         ra_dtype dtype, int32_t rotary_mode, float rope_scale, float rope_theta,
-                        float sm_scale, hipStream_t stream) {
+                        float sm_scale, int32_t num_kv_splits, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   ra_status st = check_common(q, q_indptr, out, lse, batch, total_q, h_q, h_kv, head_dim, dtype,
                               rotary_mode, sm_scale);
   if (st != RA_OK) return st;
@@ -174,8 +208,98 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
   p.rope_scale = rope_scale;
   fill_inv_freq(p.inv_freq, rotary_mode == 1, rope_theta, head_dim);
   p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
-  return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kPaged,
-                                  tree ? ra::kMaskTree : ra::kMaskCausal, stream));
+  const ra::MaskKind mask = tree ? ra::kMaskTree : ra::kMaskCausal;
+  int32_t splits = num_kv_splits;
+  if (splits < 0 || splits > kMaxSplits) return fail(RA_EINVAL, "num_kv_splits must be in [0, %d]", kMaxSplits);
+  if (splits == 0) {
+    splits = auto_splits(batch, total_q, p.group, h_kv, nnz_pages);
+    while (splits > 1 && split_workspace_bytes(total_q, h_q, head_dim, splits) > workspace_bytes) --splits;
+  } else if (splits > 1 && split_workspace_bytes(total_q, h_q, head_dim, splits) > workspace_bytes) {
+    return fail(RA_EINVAL, "workspace of %zu bytes is smaller than the %zu needed for %d splits",
+                workspace_bytes, split_workspace_bytes(total_q, h_q, head_dim, splits), splits);
+  }
+  if (splits > 1 && workspace == nullptr) return fail(RA_EINVAL, "workspace is NULL");
+  if (splits <= 1) return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kPaged, mask, stream));
+  const size_t rows = static_cast<size_t>(total_q) * h_q;
+  p.num_splits = splits;
+  p.part_out = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_out_bytes(rows, head_dim, splits));
+  hipError_t e = ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kPaged, mask, stream);
+  if (e != hipSuccess) return launched(e);
+  ra::MergeParams mp{};
+  mp.part_out = p.part_out;
+  mp.part_lse = p.part_lse;
+  mp.out = out;
+  mp.lse = lse;
+  mp.num_splits = splits;
+  mp.rows = static_cast<int32_t>(rows);
+  return launched(ra::launch_merge(mp, dtype == RA_BF16, head_dim, stream));
+}
+
+
+extern "C" {
+
+ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* pages,
+                        const int32_t* page_indptr, const int32_t* page_values,
+                        const int32_t* length_info, int32_t sliding_window,
+                        const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
+                        const int32_t* tree_order_indptr, const int32_t* tree_order,
+                        int32_t causal, void* out, float* lse, int32_t batch, int32_t total_q,
+                        int32_t num_pages, int32_t nnz_pages, int32_t tree_size,
+                        int32_t page_size, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                        ra_dtype dtype, int32_t rotary_mode, float rope_scale, float rope_theta,
+                        float sm_scale, hipStream_t stream) {
+  return paged_attn_impl(q, q_indptr, pages, page_indptr, page_values, length_info,
+                         sliding_window, k_rope_pos_offset, q_rope_position, tree_order_indptr,
+                         tree_order, causal, out, lse, batch, total_q, num_pages, nnz_pages,
+                         tree_size, page_size, h_q, h_kv, head_dim, dtype, rotary_mode,
+                         rope_scale, rope_theta, sm_scale, 1, nullptr, 0, stream);
+}
+
+size_t ra_paged_attn_split_workspace(int32_t total_q, int32_t h_q, int32_t head_dim,
+                                     int32_t num_kv_splits) {
+  return split_workspace_bytes(total_q, h_q, head_dim, std::min(num_kv_splits, kMaxSplits));
+}
+
+ra_status ra_paged_attn_split(const void* q, const int32_t* q_indptr, const void* pages,
+                              const int32_t* page_indptr, const int32_t* page_values,
+                              const int32_t* length_info, int32_t sliding_window,
+                              const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
+                              const int32_t* tree_order_indptr, const int32_t* tree_order,
+                              int32_t causal, void* out, float* lse, int32_t batch,
+                              int32_t total_q, int32_t num_pages, int32_t nnz_pages,
+                              int32_t tree_size, int32_t page_size, int32_t h_q, int32_t h_kv,
+                              int32_t head_dim, ra_dtype dtype, int32_t rotary_mode,
+                              float rope_scale, float rope_theta, float sm_scale,
+                              int32_t num_kv_splits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return paged_attn_impl(q, q_indptr, pages, page_indptr, page_values, length_info,
+                         sliding_window, k_rope_pos_offset, q_rope_position, tree_order_indptr,
+                         tree_order, causal, out, lse, batch, total_q, num_pages, nnz_pages,
+                         tree_size, page_size, h_q, h_kv, head_dim, dtype, rotary_mode,
+                         rope_scale, rope_theta, sm_scale, num_kv_splits, workspace,
+                         workspace_bytes, stream);
+}
+
+ra_status ra_merge_states(const float* part_out, const float* part_lse, int32_t num_splits,
+                          int32_t rows, int32_t head_dim, ra_dtype dtype, void* out, float* lse,
+                          hipStream_t stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(RA_EINVAL, "num_splits must be in [1, %d]", kMaxSplits);
+  if (rows < 0) return fail(RA_EINVAL, "negative rows");
+  if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported", (int)dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  if (rows == 0) return ok();
+  if (part_out == nullptr || part_lse == nullptr || out == nullptr || lse == nullptr)
+    return fail(RA_EINVAL, "a required pointer is NULL");
+  ra::MergeParams mp{};
+  mp.part_out = part_out;
+  mp.part_lse = part_lse;
+  mp.out = out;
+  mp.lse = lse;
+  mp.num_splits = num_splits;
+  mp.rows = rows;
+  return launched(ra::launch_merge(mp, dtype == RA_BF16, head_dim, stream));
 }
 
 ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append_indptr,

@@ -41,7 +41,22 @@ struct AttnParams {
   int32_t rope_q, rope_k;  // 0/1
   float rope_scale;
   float sm_scale_log2;     // sm_scale * log2(e)
+  // split-KV: num_splits > 1 splits each item's KV tiles into num_splits
+  // contiguous ranges; range s writes its normalised partial output (fp32)
+  // and lse to part_out / part_lse at [s][row] instead of out / lse.
+  int32_t num_splits;
+  float* part_out;         // [num_splits, total_q * h_q, head_dim]
+  float* part_lse;         // [num_splits, total_q * h_q]
   double inv_freq[64];     // RoPE: theta^(-2k/head_dim), k < head_dim / 2
+};
+
+// Merge of split-KV partial states into out (dtype) and lse.
+struct MergeParams {
+  const float* part_out;   // [num_splits, rows, head_dim]
+  const float* part_lse;   // [num_splits, rows]
+  void* out;               // [rows, head_dim] fp16/bf16
+  float* lse;              // [rows]
+  int32_t num_splits, rows;
 };
 
 struct AppendParams {
@@ -62,5 +77,6 @@ struct AppendParams {
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
                        MaskKind mask, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int is_bf16, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int is_bf16, int head_dim, hipStream_t stream);
 
 }  // namespace ra

@@ -1,6 +1,6 @@
 """Benchmark: ragged, batched, masked GQA attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k|name] [--split S]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
@@ -9,7 +9,10 @@ one launch of the attention kernel (work partition, Q load + RoPE, K/V gather
 are resident in HBM before the timed region. Default workload: the batched
 tree-attention configuration (16 trees of 64 nodes, h_q 32 / h_kv 8, d 128,
 fp16, inline RoPE theta 1e4). Other workloads (--config 0..4) print the same
-line for that workload.
+line for that workload; `--config paged_decode` times the split-KV entry point
+(ra_paged_attn_split, one step = the attention kernel + the merge kernel) on a
+decode batch, `--split S` picks its split count (0: chosen by the library,
+-1: the unsplit entry point).
 
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
@@ -226,7 +229,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--config", default=str(DEFAULT_CONFIG),
+                    help="0..4, or an extra workload name (paged_decode)")
+    ap.add_argument("--split", type=int, default=None,
+                    help="split-KV count for paged workloads (0: auto, -1: unsplit entry point); "
+                         "default: auto for paged_decode, unsplit otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graph-launches", type=int, default=100,
@@ -246,19 +253,25 @@ def main():
         return
 
     import attention_ragged_gqa_amd as ra
-    from workloads import make_config
+    from workloads import EXTRA_NAMES, make_config, make_extra
     from workloads.device import DeviceInputs
 
     ra.library()
     t_gen = time.perf_counter()
-    w = make_config(args.config)
+    w = make_extra(args.config) if args.config in EXTRA_NAMES else make_config(int(args.config))
+    split = args.split
+    if split is None:
+        split = 0 if args.config in EXTRA_NAMES else -1
+    if split >= 0 and w.kind == "tree":
+        split = -1
+    launch_kw = {} if split < 0 else {"num_kv_splits": split}
     log("[bench] generated %s in %.1fs" % (w.name, time.perf_counter() - t_gen))
     di = DeviceInputs(w, "cuda:0")
     torch.cuda.synchronize()
     log("[bench] inputs resident on cuda:0")
 
     for _ in range(args.warmup):
-        di.launch()
+        di.launch(**launch_kw)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()       # the stream the kernel is launched on
@@ -274,7 +287,7 @@ def main():
         torch.cuda.synchronize()
         ev0.record(stream)
         for _ in range(eager_steps):
-            di.launch()
+            di.launch(**launch_kw)
         ev1.record(stream)
         torch.cuda.synchronize()
         ms_eager = ev0.elapsed_time(ev1) / eager_steps
@@ -287,7 +300,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(n):
-                di.launch()
+                di.launch(**launch_kw)
         return g
 
     if use_graph:
@@ -304,7 +317,7 @@ def main():
             g_rem.replay()
     else:   # eager launches only (--graph-launches 0)
         for _ in range(args.steps):
-            di.launch()
+            di.launch(**launch_kw)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -341,7 +354,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if w.dtype == "f16" else "bf16", "data": "synthetic",
-        "config": config_summary(w), "tokens_per_s": round(tokens_s, 1),
+        "config": dict(config_summary(w), **({"kv_splits": "auto" if split == 0 else split}
+                                               if split >= 0 else {})),
+        "tokens_per_s": round(tokens_s, 1),
         "fractions": {"mfma": round(mfma_frac, 4), "hbm": round(hbm_frac, 4)},
         "unmasked_pairs": pairs, "roofline": roof,
         "timing": {"mode": "hip_graph_replay" if use_graph else "eager", "launches_per_graph": per_graph,

@@ -37,6 +37,7 @@
 #ifndef RAGATTN_H
 #define RAGATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -119,6 +120,62 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
                         int32_t page_size, int32_t h_q, int32_t h_kv, int32_t head_dim,
                         ra_dtype dtype, int32_t rotary_mode, float rope_scale, float rope_theta,
                         float sm_scale, hipStream_t stream);
+
+/*
+ * Split-KV form of ra_paged_attn, for few query rows over long KV (decode).
+ * Same arguments and result as ra_paged_attn, plus:
+ *   num_kv_splits   1..64: each work item's KV tiles are cut into this many
+ *                   contiguous ranges, processed by separate workgroups;
+ *                   0: chosen by the library (about four work items per
+ *                   compute unit, at least two 64-key tiles per range on the
+ *                   mean sequence, limited by the workspace); 1: no split.
+ *   workspace       caller-owned device memory for the partial states,
+ *                   at least ra_paged_attn_split_workspace(...) bytes for the
+ *                   split count used (may be NULL when that is 0).
+ * Each range writes its normalised output (fp32) and base-2 lse; a second
+ * kernel merges them (see ra_merge_states). The merge is the online-softmax
+ * update of the "_kernel_common.py" page applied to whole ranges; the base-2
+ * lse that the page's epilogue stores is what makes the ranges combinable.
+ * Errors as ra_paged_attn, and RA_EINVAL for num_kv_splits outside [0, 64]
+ * or a workspace smaller than the explicit split count needs. Both kernels
+ * run on `stream`; the workspace must stay valid until they finish. With
+ * more than one split every row of out/lse is written by the merge, so
+ * q_indptr[batch] must equal total_q (rows outside every sequence would get
+ * unspecified values).
+ */
+ra_status ra_paged_attn_split(const void* q, const int32_t* q_indptr, const void* pages,
+                              const int32_t* page_indptr, const int32_t* page_values,
+                              const int32_t* length_info, int32_t sliding_window,
+                              const int32_t* k_rope_pos_offset, const int32_t* q_rope_position,
+                              const int32_t* tree_order_indptr, const int32_t* tree_order,
+                              int32_t causal, void* out, float* lse, int32_t batch,
+                              int32_t total_q, int32_t num_pages, int32_t nnz_pages,
+                              int32_t tree_size, int32_t page_size, int32_t h_q, int32_t h_kv,
+                              int32_t head_dim, ra_dtype dtype, int32_t rotary_mode,
+                              float rope_scale, float rope_theta, float sm_scale,
+                              int32_t num_kv_splits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Bytes of workspace ra_paged_attn_split needs for num_kv_splits ranges
+ * (0 when num_kv_splits <= 1): num_kv_splits * total_q * h_q * (head_dim + 1)
+ * floats, the output part rounded up to 256 bytes. */
+size_t ra_paged_attn_split_workspace(int32_t total_q, int32_t h_q, int32_t head_dim,
+                                     int32_t num_kv_splits);
+
+/*
+ * Merge partial attention states over disjoint KV ranges:
+ *   part_out [num_splits, rows, head_dim] fp32, each row normalised over its
+ *   range; part_lse [num_splits, rows] fp32 base-2 lse of the range (-inf for
+ *   a range with no visible key).
+ * Writes lse[r] = log2 sum_s 2^part_lse[s][r] and
+ * out[r] = sum_s 2^(part_lse[s][r] - lse[r]) * part_out[s][r] in `dtype`
+ * (rows with no visible key anywhere: out 0, lse -inf). rows = tokens * heads
+ * of a [tokens, heads, head_dim] output. Errors: RA_EINVAL (num_splits not in
+ * [1, 64], negative rows, NULL pointers), RA_EUNSUPPORTED (head_dim, dtype).
+ */
+ra_status ra_merge_states(const float* part_out, const float* part_lse, int32_t num_splits,
+                          int32_t rows, int32_t head_dim, ra_dtype dtype, void* out, float* lse,
+                          hipStream_t stream);
 
 /*
  * Append new K/V tokens into the paged cache, rotating K first when

@@ -15,7 +15,8 @@ precision it follows them: the rotary embedding is evaluated in float32 and
 rounded to the storage dtype.
 
 Modules:
-  attention -- vectorised float64 oracle (tree_attn, paged_attn, rope, masks)
+  attention -- vectorised float64 oracle (tree_attn, paged_attn, rope, masks,
+               merge_states for split key sets)
   scalar    -- pure-Python brute force for tiny inputs (ancestor sets from
                parent pointers rather than DFS intervals)
 """
@@ -25,6 +26,7 @@ from .attention import (  # noqa: F401
     attend,
     causal_visible,
     kv_chunk_len,
+    merge_states,
     paged_attn,
     rope,
     rope_exact,

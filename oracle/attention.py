@@ -188,6 +188,32 @@ def attend(qr: np.ndarray, kr: np.ndarray, vr: np.ndarray, vis: np.ndarray, sm_s
     return out, lse
 
 
+def merge_states(part_out: np.ndarray, part_lse: np.ndarray):
+    """Combine attention states over disjoint key sets.
+
+    part_out [S, R, D] (each row normalised over its own key set), part_lse
+    [S, R] base-2 log-sum-exp (-inf for an empty set). Since each part is
+    out_s = sum_{j in K_s} e^{s_j} v_j / sum_{j in K_s} e^{s_j} with
+    sum_{j in K_s} e^{s_j} = 2^{lse_s}, the union gives
+    lse = log2 sum_s 2^{lse_s} and out = sum_s 2^{lse_s - lse} out_s
+    (the online-softmax update of the "_kernel_common.py" page applied to
+    whole key sets). Rows empty in every part: out 0, lse -inf."""
+    part_out = np.asarray(part_out, dtype=np.float64)
+    part_lse = np.asarray(part_lse, dtype=np.float64)
+    S, R, D = part_out.shape
+    out = np.zeros((R, D), dtype=np.float64)
+    lse = np.full(R, -np.inf, dtype=np.float64)
+    has = np.isfinite(part_lse).any(axis=0)
+    if not has.any():
+        return out, lse
+    m = np.max(np.where(np.isfinite(part_lse[:, has]), part_lse[:, has], -np.inf), axis=0)
+    w = np.exp2(part_lse[:, has] - m)                      # [S, R'] (0 for empty parts)
+    tot = w.sum(axis=0)
+    lse[has] = m + np.log2(tot)
+    out[has] = np.einsum("sr,srd->rd", w / tot, part_out[:, has, :])
+    return out, lse
+
+
 def _select_tokens(q_indptr, rows: Optional[np.ndarray], b: int) -> np.ndarray:
     """Query indices (within sequence b) to evaluate."""
     q0, q1 = int(q_indptr[b]), int(q_indptr[b + 1])

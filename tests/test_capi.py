@@ -119,6 +119,46 @@ def test_paged_attn_rejects(lib, kw, status):
     assert ra.ra_last_error() != ""
 
 
+def _split(lib, splits, ws_bytes, ws=ctypes.c_void_p(0x2000), **kw):
+    a = dict(sliding=0, causal=1, batch=1, total_q=4, num_pages=4, nnz=4, tree_size=0, page=16,
+             h_q=8, h_kv=2, d=128, dtype=1, rot=0, scale=1.0, theta=1e4, sm=0.1)
+    a.update(kw)
+    P = ctypes.c_void_p(0x1000)
+    return lib.ra_paged_attn_split(P, P, P, P, P, P, a["sliding"], None, None, None, None,
+                                   a["causal"], P, P, a["batch"], a["total_q"], a["num_pages"],
+                                   a["nnz"], a["tree_size"], a["page"], a["h_q"], a["h_kv"], a["d"],
+                                   a["dtype"], a["rot"], a["scale"], a["theta"], a["sm"], splits,
+                                   ws, ws_bytes, None)
+
+
+def test_split_workspace_size(lib):
+    # splits * rows * (d + 1) floats, the output part rounded up to 256 bytes
+    assert ra.ra_paged_attn_split_workspace(4, 8, 128, 1) == 0
+    assert ra.ra_paged_attn_split_workspace(4, 8, 128, 3) == 3 * 32 * 128 * 4 + 3 * 32 * 4
+    assert ra.ra_paged_attn_split_workspace(5, 3, 64, 2) == (2 * 15 * 64 * 4 + 255) // 256 * 256 + 2 * 15 * 4
+    assert ra.ra_paged_attn_split_workspace(0, 8, 128, 4) == 0
+
+
+def test_split_rejects(lib):
+    need = ra.ra_paged_attn_split_workspace(4, 8, 128, 4)
+    assert _split(lib, 65, 1 << 20) == ra.RA_EINVAL             # too many splits
+    assert _split(lib, -1, 1 << 20) == ra.RA_EINVAL
+    assert _split(lib, 4, need - 1) == ra.RA_EINVAL             # explicit count, workspace too small
+    assert _split(lib, 4, need, ws=None) == ra.RA_EINVAL        # NULL workspace
+    assert _split(lib, 4, need, d=96) == ra.RA_EUNSUPPORTED     # same checks as ra_paged_attn
+    assert _split(lib, 4, need, batch=0, total_q=0) == ra.RA_OK  # nothing to do, no launch
+
+
+def test_merge_rejects(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.ra_merge_states(P, P, 0, 4, 128, 1, P, P, None) == ra.RA_EINVAL
+    assert lib.ra_merge_states(P, P, 65, 4, 128, 1, P, P, None) == ra.RA_EINVAL
+    assert lib.ra_merge_states(P, P, 2, -1, 128, 1, P, P, None) == ra.RA_EINVAL
+    assert lib.ra_merge_states(P, P, 2, 4, 96, 1, P, P, None) == ra.RA_EUNSUPPORTED
+    assert lib.ra_merge_states(None, P, 2, 4, 128, 1, P, P, None) == ra.RA_EINVAL
+    assert lib.ra_merge_states(P, P, 2, 0, 128, 1, P, P, None) == ra.RA_OK
+
+
 def test_append_rejects(lib):
     P = ctypes.c_void_p(0x1000)
     st = lib.ra_paged_kv_append(P, P, P, P, None, P, P, P, 0, 5, 4, 4, 16, 2, 128, 1, 1.0, 1e4, None)

@@ -186,3 +186,65 @@ def test_graph_replay_matches_eager():
             assert torch.equal(di.out, out_e) and torch.equal(di.lse, lse_e), "replay %d differs" % rep
             di.launch()          # eager work between replays
             torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# split-KV (few query rows over long KV) and the state merge
+# ---------------------------------------------------------------------------
+
+SPLIT_CASES = {
+    "decode_causal_bf16": dict(seed=40, qo=[1, 3, 16, 1, 0], kv=[3000, 700, 5000, 64, 900], h_q=32,
+                               h_kv=8, d=128, dtype="bf16", causal=1),
+    "decode_noncausal_f16_d64": dict(seed=41, qo=[2, 5], kv=[1500, 2100], h_q=16, h_kv=2, d=64,
+                                     dtype="f16", causal=0),
+    "decode_sliding": dict(seed=42, qo=[4, 1], kv=[9000, 5000], h_q=16, h_kv=4, d=128, dtype="bf16",
+                           causal=1, sliding=([9000 - 2048, 5000 - 1024], [4, 0])),
+    "decode_tree": dict(seed=43, qo=[12, 30], kv=[1200, 800], h_q=16, h_kv=4, d=128, dtype="bf16",
+                        causal=0, tree=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_CASES))
+@pytest.mark.parametrize("splits", [2, 7, 0])
+def test_split_kv_matches_oracle(case, splits):
+    c = dict(SPLIT_CASES[case])
+    seed, qo, kv = c.pop("seed"), c.pop("qo"), c.pop("kv")
+    w = make_custom_paged(seed, qo, kv, **c)
+    say("[gpu] split-KV %s splits=%d" % (case, splits))
+    di = DeviceInputs(w)
+    out, lse = di.launch(num_kv_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = run_oracle(w)
+    d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="%s/%d" % (case, splits))
+    say("[gpu] split-KV %s splits=%d: max|d out| %.2e max rel|d lse| %.2e" % (case, splits, d_out, d_lse))
+
+
+def test_merge_states_matches_oracle():
+    rng = np.random.default_rng(44)
+    S, rows, d = 5, 300, 128
+    po = rng.standard_normal((S, rows, d)).astype(np.float32)
+    pl = (rng.standard_normal((S, rows)) * 4).astype(np.float32)
+    pl[1, :40] = -np.inf                 # empty ranges
+    pl[:, 50] = -np.inf                  # a row with no visible key anywhere
+    import attention_ragged_gqa_amd as ra
+    for dtype in (torch.bfloat16, torch.float16):
+        out = torch.empty(rows, d, dtype=dtype, device="cuda")
+        lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+        ra.ra_merge_states(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, lse)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.merge_states(po.astype(np.float64), pl.astype(np.float64))
+        compare(out, lse, ref_o, ref_l, label="merge %s" % dtype)
+
+
+def test_paged_decode_full_size_split():
+    """The decode workload the benchmark times with split-KV, every row, both
+    entry points."""
+    from workloads import make_extra
+    w = make_extra("paged_decode")
+    ref_out, ref_lse = run_oracle(w)
+    di = DeviceInputs(w)
+    for splits in (None, 0):
+        say("[gpu] paged_decode splits=%s" % splits)
+        out, lse = di.launch() if splits is None else di.launch(num_kv_splits=splits)
+        torch.cuda.synchronize()
+        compare(out, lse, ref_out, ref_lse, label="paged_decode/%s" % splits)

@@ -413,3 +413,40 @@ def test_row_sampling_matches_full():
     np.testing.assert_array_equal(out[rows], out2[rows])
     others = np.setdiff1d(np.arange(w.total_q), rows)
     assert np.isnan(out2[others]).all()
+
+
+# ---------------------------------------------------------------------------
+# merge of states over disjoint key sets (split-KV)
+# ---------------------------------------------------------------------------
+
+def test_merge_of_split_key_sets_equals_attention_over_the_union():
+    """Attention over a key set equals the merge of attention over any
+    partition of it (pinned against the unsplit definition, which the other
+    pins tie to SDPA); empty parts and fully empty rows included."""
+    rng = np.random.default_rng(7)
+    R, L, D = 6, 40, 16
+    q = rng.standard_normal((R, D)); k = rng.standard_normal((L, D)); v = rng.standard_normal((L, D))
+    vis = rng.random((R, L)) < 0.6
+    vis[3] = False                      # no visible key at all
+    vis[4, :] = False; vis[4, 35] = True   # one key, in the last part
+    ref_o, ref_l = oracle.attend(q, k, v, vis, 0.3)
+    cuts = [0, 7, 7, 20, 33, 40]        # includes an empty part
+    parts = [oracle.attend(q, k[a:b], v[a:b], vis[:, a:b], 0.3) for a, b in zip(cuts[:-1], cuts[1:])]
+    po = np.stack([p[0] for p in parts]); pl = np.stack([p[1] for p in parts])
+    o, l = oracle.merge_states(po, pl)
+    assert np.isneginf(l[3]) and np.all(o[3] == 0)
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(l[fin], ref_l[fin], rtol=0, atol=1e-12)
+    # a single part is the identity
+    o1, l1 = oracle.merge_states(ref_o[None], ref_l[None])
+    np.testing.assert_array_equal(o1, ref_o)
+
+
+def test_merge_two_equal_halves_closed_form():
+    """Two parts with equal lse: lse + 1 (base 2) and the mean of the outputs."""
+    po = np.array([[[1.0, -2.0]], [[3.0, 4.0]]])
+    pl = np.array([[0.5], [0.5]])
+    o, l = oracle.merge_states(po, pl)
+    np.testing.assert_allclose(l, [1.5], atol=1e-15)
+    np.testing.assert_allclose(o, [[2.0, 1.0]], atol=1e-15)

@@ -10,11 +10,13 @@ and the oracle compute those on their own.
 
 from .generators import (  # noqa: F401
     CONFIG_NAMES,
+    EXTRA_NAMES,
     Workload,
     dfs_intervals,
     make_config,
     make_custom_paged,
     make_custom_tree,
+    make_extra,
     pages_from_logical,
     random_tree,
 )

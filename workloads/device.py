@@ -61,9 +61,25 @@ class DeviceInputs:
             self.tree_order_indptr = _i32(w.tree_order_indptr, d)
             self.tree_order = _i32(None if w.tree_order is None else w.tree_order.reshape(-1, 2), d)
 
-    def launch(self, stream=None):
+    def launch(self, stream=None, num_kv_splits=None):
+        """One launch; num_kv_splits (paged only) selects the split-KV entry
+        point (0: the library chooses the count)."""
         import attention_ragged_gqa_amd as ra
         w = self.w
+        if num_kv_splits is not None:
+            if w.kind == "tree":
+                raise ValueError("split-KV is a paged entry point")
+            if getattr(self, "workspace", None) is None:
+                n = ra.ra_paged_attn_split_workspace(w.total_q, w.h_q, w.d, 64)
+                self.workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
+            return ra.ra_paged_attn_split(
+                self.q, self.q_indptr, self.pages, self.page_indptr, self.page_values,
+                self.length_info, sliding_window=w.sliding_window,
+                k_rope_pos_offset=self.k_rope_pos_offset, q_rope_position=self.q_rope_position,
+                tree_order_indptr=self.tree_order_indptr, tree_order=self.tree_order,
+                causal=w.causal, out=self.out, lse=self.lse, rotary_mode=w.rotary_mode,
+                rope_scale=w.rope_scale, rope_theta=w.rope_theta, sm_scale=w.sm_scale,
+                num_kv_splits=num_kv_splits, workspace=self.workspace, stream=stream)
         if w.kind == "tree":
             return ra.ra_tree_attn(self.q, self.q_indptr, self.k, self.v, self.kv_indptr,
                                    self.q_rope_position, self.mn_indptr, self.tree_mask,

@@ -325,6 +325,26 @@ def make_custom_paged(seed: int, qo_lens, stored_lens, h_q: int, h_kv: int, d: i
     return w
 
 
+# Workloads beyond the five configurations, for entry points adjacent to
+# the main path (split-KV decode).
+EXTRA_NAMES = ("paged_decode",)
+
+
+def make_extra(name: str, seed: Optional[int] = None) -> Workload:
+    """paged_decode: 16 sequences decoding one token each over 8K-24K cached
+    tokens (K rotated when cached, pages permuted), h_q 32 / h_kv 8, d 128,
+    bf16, causal. Seed 2000."""
+    if name != "paged_decode":
+        raise KeyError(name)
+    seed = 2000 if seed is None else seed
+    rng = _rng(seed)
+    b = 16
+    stored = rng.integers(8192, 24577, size=b)
+    return make_custom_paged(seed, [1] * b, stored, h_q=32, h_kv=8, d=128, dtype="bf16",
+                             causal=1, store_rope="linear", rotary_mode=0, rope_theta=1e4,
+                             name=name, rng=rng)
+
+
 def make_config(k: int, seed: Optional[int] = None) -> Workload:
     """The five workloads, by 0-based index into CONFIG_NAMES. Seed 1000 + k."""
     name = CONFIG_NAMES[k]

@@ -25,6 +25,7 @@ __all__ = [
     "EXPORTED_SYMBOLS",
     "ra_tree_attn",
     "ra_paged_attn",
+    "ra_ragged_prefill",
     "ra_paged_attn_split",
     "ra_paged_attn_split_workspace",
     "ra_merge_states",
@@ -35,7 +36,7 @@ __all__ = [
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libragattn.so"
 
-EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_paged_attn_split",
+EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
                     "ra_paged_attn_split_workspace", "ra_merge_states", "ra_paged_kv_append",
                     "ra_last_error")
 
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
     lib.ra_paged_attn.restype = i32
     lib.ra_paged_attn.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
                                   + [i32, i32, f32, f32, f32, vp])
+    lib.ra_ragged_prefill.restype = i32
+    lib.ra_ragged_prefill.argtypes = [vp] * 6 + [i32, i32, vp, vp] + [i32] * 7 + [f32, vp]
     lib.ra_paged_attn_split.restype = i32
     lib.ra_paged_attn_split.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
                                         + [i32, i32, f32, f32, f32, i32, vp, ctypes.c_size_t, vp])
@@ -204,6 +207,35 @@ def ra_paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info,
         q_indptr.numel() - 1, total_q, num_pages, page_values.numel(), tree_size, page_size,
         h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
         _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len=None, pad_mode: int = 0,
+                      causal: int = 1, out=None, lse=None, sm_scale: Optional[float] = None,
+                      stream=None):
+    """Ragged prefill over contiguous K/V with optional padded-batch masks
+    (C: ra_ragged_prefill). q [total_q, h_q, d], k/v [total_kv, h_kv, d];
+    pad_mode 0 plain (causal or not), 1 right padding (non-causal),
+    2 left padding (causal) with valid_len [b]. Returns (out, lse)."""
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("kv_indptr", kv_indptr), ("valid_len", valid_len)):
+        _check_dev(name, t, i32, dev)
+    out, lse = _out_lse(q, out, lse)
+    total_q, h_q, d = q.shape
+    total_kv, h_kv = k.shape[0], k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    st = library().ra_ragged_prefill(
+        _ptr(q), _ptr(q_indptr), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(valid_len), int(pad_mode),
+        int(causal), _ptr(out), _ptr(lse), q_indptr.numel() - 1, total_q, total_kv, h_q, h_kv, d,
+        _DTYPES[q.dtype], sm_scale, _stream(dev, stream))
     _raise(st)
     return out, lse
 

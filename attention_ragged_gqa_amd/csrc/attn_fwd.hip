@@ -108,6 +108,9 @@ __device__ __forceinline__ void wait_all_and_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 }
 
+// First token of the 128-row tile starting at packed row row0.
+__device__ __forceinline__ int t_first_of(int row0, int g) { return row0 / g; }
+
 // Locate this workgroup's work item. Returns false when the block has none.
 // Item list: for each KV head, for each sequence b (in order), ranks
 // 0..tiles_b-1 with rank 0 = the last (heaviest under a causal mask) q-tile.
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // The per-sequence scalars come in one vector load (lane i fetches value i)
   // and are read back with v_readlane: one round trip instead of a chain.
   int kv_len_m = 0, kv_base_m = 0, page_base_m = 0, page_end_m = 0, sink_m = 0, win_off_m = 0;
-  int li0 = 0, li1 = 0, li2 = 0, pi1 = 0, ti0 = 0, ti1 = 0, kp0 = 0;
+  int li0 = 0, li1 = 0, li2 = 0, pi1 = 0, ti0 = 0, ti1 = 0, kp0 = 0, valid_m = 0;
   {
     const int32_t* src = q_indptr_ + b;   // any valid address for unused lanes
     if constexpr (LAYOUT == kContiguous) {
@@ -274,6 +277,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     if constexpr (MASK == kMaskTree) {
       if (lane == 5) src = tree_indptr_ + b;
       if (lane == 6) src = tree_indptr_ + b + 1;
+    }
+    if constexpr (MASK == kMaskCausal) {
+      if (p.pad_mode != 0) valid_m = p.valid_len[b];   // uniform
     }
     const int v = *src;
     if constexpr (LAYOUT == kContiguous) {
@@ -325,14 +331,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const int t_hi = min((row0 + w * 32 + 31) / g, qo_len - 1);
   const bool wave_active = t_lo < qo_len;
 
+  // Causal-or-none masks: row t sees keys [lo, lim) of the chunk (lo > 0
+  // only with left padding). lim_lo / lim_hi (and lo_min / lo_max) bound
+  // them over the wave's rows for the per-tile classification.
   const bool causal = (MASK == kMaskCausal) && causal_;
-  const int lim = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
-  const int lim_lo = causal ? min(kv_len, kv_len - qo_len + t_lo + 1) : kv_len;
-  const int lim_hi = causal ? min(kv_len, kv_len - qo_len + t_hi + 1) : kv_len;
+  const int pad_mode = MASK == kMaskCausal ? p.pad_mode : 0;
+  int lim_m = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
+  int lo_m = 0;
   int kv_hi = kv_len;
-  if (causal) {
-    const int t_last = min((row0 + kBM - 1) / g, qo_len - 1);
-    kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
+  const int t_last = min((row0 + kBM - 1) / g, qo_len - 1);
+  if (causal) kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
+  if (pad_mode == 1) {          // right padding: rows and keys below valid_len
+    const int vl = min(max(valid_m, 0), kv_len);
+    lim_m = (t < valid_m) ? min(lim_m, vl) : 0;
+    kv_hi = (t_first_of(row0, g) < valid_m) ? min(kv_hi, vl) : 0;
+  } else if (pad_mode == 2) {   // left padding, causal: valid suffixes
+    const int vq = min(max(valid_m, 0), qo_len), vk = min(max(valid_m, 0), kv_len);
+    lo_m = kv_len - vk;
+    if (t < qo_len - vq) lim_m = 0;
+  }
+  const int lim = lim_m, lo = lo_m;
+  int lim_lo = causal ? min(kv_len, kv_len - qo_len + t_lo + 1) : kv_len;
+  int lim_hi = causal ? min(kv_len, kv_len - qo_len + t_hi + 1) : kv_len;
+  int lo_min = 0, lo_max = 0;
+  if (pad_mode != 0) {
+    // per-wave bounds by reduction over the wave's valid rows (uniform)
+    const bool in_seq = t < qo_len;
+    int hmin = in_seq ? lim : INT_MAX, hmax = in_seq ? lim : INT_MIN;
+    int lmin = in_seq ? lo : INT_MAX, lmax = in_seq ? lo : INT_MIN;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      hmin = min(hmin, __shfl_xor(hmin, m, 64));
+      hmax = max(hmax, __shfl_xor(hmax, m, 64));
+      lmin = min(lmin, __shfl_xor(lmin, m, 64));
+      lmax = max(lmax, __shfl_xor(lmax, m, 64));
+    }
+    lim_lo = __builtin_amdgcn_readfirstlane(hmin);
+    lim_hi = __builtin_amdgcn_readfirstlane(hmax);
+    lo_min = __builtin_amdgcn_readfirstlane(lmin);
+    lo_max = __builtin_amdgcn_readfirstlane(lmax);
   }
   const int n_tiles_all = kv_hi > 0 ? (kv_hi + kBN - 1) / kBN : 0;
   // split-KV: this item's contiguous range of those tiles
@@ -815,13 +852,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
           for (int r = 0; r < 16; ++r)
             if (!((vbits >> (16 * kb + r)) & 1u)) sacc[kb][r] = -INFINITY;
       } else {
-        // key j0 + 4hh + c(kb, r) is visible iff c < lim - j0 - 4hh
+        // key j0 + 4hh + c(kb, r) is visible iff lo - j0 - 4hh <= c < lim - j0 - 4hh
         const int rel = lim - j0 - 4 * hh;
+        if (lo_max == 0) {   // uniform: no lower bound (always, without left padding)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) sacc[kb][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r)
+              if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) sacc[kb][r] = -INFINITY;
+        } else {
+          const int rel_lo = lo - j0 - 4 * hh;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+              if ((c >= rel) | (c < rel_lo)) sacc[kb][r] = -INFINITY;
+            }
+        }
       }
     }
     float mx = -INFINITY;
@@ -897,7 +945,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     if constexpr (MASK == kMaskTree) {
       cls = (j0 + kBN <= min(tree_start, kv_len)) ? 1 : 2;
     } else {
-      cls = (j0 >= lim_hi) ? 0 : ((j0 + kBN <= lim_lo) ? 1 : 2);
+      cls = (j0 >= lim_hi || j0 + kBN <= lo_min) ? 0
+                                                : ((j0 + kBN <= lim_lo && j0 >= lo_max) ? 1 : 2);
     }
     cls = __builtin_amdgcn_readfirstlane(cls);
     if (wave_active && cls != 0) compute(j0, cls == 2);

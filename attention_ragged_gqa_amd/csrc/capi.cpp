@@ -256,6 +256,45 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
                          rope_scale, rope_theta, sm_scale, 1, nullptr, 0, stream);
 }
 
+ra_status ra_ragged_prefill(const void* q, const int32_t* q_indptr, const void* k, const void* v,
+                            const int32_t* kv_indptr, const int32_t* valid_len, int32_t pad_mode,
+                            int32_t causal, void* out, float* lse, int32_t batch,
+                            int32_t total_q, int32_t total_kv, int32_t h_q, int32_t h_kv,
+                            int32_t head_dim, ra_dtype dtype, float sm_scale,
+                            hipStream_t stream) {
+  ra_status st = check_common(q, q_indptr, out, lse, batch, total_q, h_q, h_kv, head_dim, dtype, 0,
+                              sm_scale);
+  if (st != RA_OK) return st;
+  if (total_kv < 0) return fail(RA_EINVAL, "negative total_kv");
+  if (batch > 0 && kv_indptr == nullptr) return fail(RA_EINVAL, "kv_indptr is NULL");
+  if (total_kv > 0 && (k == nullptr || v == nullptr)) return fail(RA_EINVAL, "k and v must be non-NULL");
+  if (pad_mode < 0 || pad_mode > 2) return fail(RA_EINVAL, "pad_mode must be 0, 1 or 2, got %d", pad_mode);
+  if (pad_mode != 0 && batch > 0 && valid_len == nullptr) return fail(RA_EINVAL, "valid_len is NULL");
+  if (pad_mode == 1 && causal != 0) return fail(RA_EINVAL, "pad_mode 1 (right padding) is not causal");
+  if (pad_mode == 2 && causal == 0) return fail(RA_EINVAL, "pad_mode 2 (left padding) is causal");
+  if (batch == 0 || total_q == 0) return ok();
+  ra::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_indptr = q_indptr;
+  p.out = out;
+  p.lse = lse;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.kv_indptr = kv_indptr;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.total_kv = total_kv;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.group = h_q / h_kv;
+  p.causal = causal != 0;
+  p.valid_len = valid_len;
+  p.pad_mode = pad_mode;
+  p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  return launched(ra::launch_attn(p, dtype == RA_BF16, head_dim, ra::kContiguous, ra::kMaskCausal,
+                                  stream));
+}
+
 size_t ra_paged_attn_split_workspace(int32_t total_q, int32_t h_q, int32_t head_dim,
                                      int32_t num_kv_splits) {
   return split_workspace_bytes(total_q, h_q, head_dim, std::min(num_kv_splits, kMaxSplits));

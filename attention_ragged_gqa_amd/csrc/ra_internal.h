@@ -41,6 +41,12 @@ struct AttnParams {
   int32_t rope_q, rope_k;  // 0/1
   float rope_scale;
   float sm_scale_log2;     // sm_scale * log2(e)
+  // padded batches (causal-or-none masks only): pad_mode 1 = right padding,
+  // query row t and key j visible iff t < valid_len[b] and j < valid_len[b];
+  // pad_mode 2 = left padding with causal alignment, queries
+  // [qo_len - valid, qo_len) and keys [kv_len - valid, kv_len) are real
+  const int32_t* valid_len;
+  int32_t pad_mode;
   // split-KV: num_splits > 1 splits each item's KV tiles into num_splits
   // contiguous ranges; range s writes its normalised partial output (fp32)
   // and lse to part_out / part_lse at [s][row] instead of out / lse.

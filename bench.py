@@ -12,7 +12,8 @@ fp16, inline RoPE theta 1e4). Other workloads (--config 0..4) print the same
 line for that workload; `--config paged_decode` times the split-KV entry point
 (ra_paged_attn_split, one step = the attention kernel + the merge kernel) on a
 decode batch, `--split S` picks its split count (0: chosen by the library,
--1: the unsplit entry point).
+-1: the unsplit entry point); `--config ragged_left_padded` times
+ra_ragged_prefill on left-padded causal prompts.
 
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
@@ -64,7 +65,7 @@ def log(*a):
 
 def chunk_lengths(w) -> np.ndarray:
     """KV columns of each sequence's chunk."""
-    if w.kind == "tree":
+    if w.kind in ("tree", "ragged"):
         return np.diff(w.kv_indptr).astype(np.int64)
     stored = np.diff(w.kv_store_indptr).astype(np.int64)
     if not w.sliding_window:
@@ -76,12 +77,22 @@ def chunk_lengths(w) -> np.ndarray:
 def visible_pairs(w) -> int:
     """Unmasked (query row, query head, key) triples. Trees: a node sees its
     depth+1 ancestors-or-self plus the whole prefix; causal: row t of qo sees
-    min(L, L - qo + t + 1) columns of an L-column chunk."""
+    min(L, L - qo + t + 1) columns of an L-column chunk; padded batches
+    restrict rows and columns to the valid prefix (right) or suffix (left)."""
     L = chunk_lengths(w)
     qo = np.diff(w.q_indptr).astype(np.int64)
     total = 0
     for b in range(w.batch):
         if qo[b] == 0:
+            continue
+        if w.kind == "ragged" and w.pad_mode != 0:
+            v = int(w.valid_len[b])
+            if w.pad_mode == 1:
+                total += max(0, min(v, qo[b])) * max(0, min(v, L[b]))
+            else:
+                vq, vk = max(0, min(v, qo[b])), max(0, min(v, L[b]))
+                t = np.arange(qo[b] - vq, qo[b])
+                total += int(np.sum(np.clip(np.minimum(L[b], L[b] - qo[b] + t + 1) - (L[b] - vk), 0, None)))
             continue
         if w.kind == "tree" or w.tree_order is not None:
             depth = np.asarray(w.depths[b], np.int64)
@@ -103,11 +114,16 @@ def algorithmic_bytes(w) -> int:
     qo = np.diff(w.q_indptr).astype(np.int64)
     L = chunk_lengths(w)
     kv_rows = int(np.sum(np.where(qo > 0, L, 0)))
+    if w.kind == "ragged" and w.pad_mode != 0:   # only the valid rows are read
+        v = np.asarray(w.valid_len, np.int64)
+        kv_rows = int(np.sum(np.where(np.minimum(v, qo) > 0, np.clip(np.minimum(v, L), 0, None), 0)))
     nbytes = 2 * total_q * w.h_q * w.d * esz + total_q * w.h_q * 4
     nbytes += kv_rows * w.h_kv * w.d * 2 * esz
     nbytes += 4 * (w.batch + 1) * 2                       # q_indptr + kv/page indptr
     if w.kind == "tree":
         nbytes += 4 * (w.batch + 1) + 8 * len(w.tree_mask)
+    elif w.kind == "ragged":
+        nbytes += 4 * w.batch if w.pad_mode != 0 else 0
     else:
         nbytes += 4 * int(np.sum((L + 15) // 16)) + 4 * np.asarray(w.length_info).size
         if w.tree_order is not None:
@@ -121,13 +137,17 @@ def config_summary(w) -> dict:
     qo = np.diff(w.q_indptr)
     c = {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
          "total_q": w.total_q, "qo_len_range": [int(qo.min()), int(qo.max())],
-         "kv_layout": "contiguous" if w.kind == "tree" else "paged16",
-         "mask": "tree" if (w.kind == "tree" or w.tree_order is not None) else
+         "kv_layout": "contiguous" if w.kind in ("tree", "ragged") else "paged16",
+         "mask": {1: "right-padded", 2: "left-padded causal"}[w.pad_mode]
+                 if (w.kind == "ragged" and w.pad_mode) else
+                 "tree" if (w.kind == "tree" or w.tree_order is not None) else
                  ("sliding+causal" if w.sliding_window else ("causal" if w.causal else "none")),
          "rope": ("inline q/k theta=%g" % w.rope_theta) if (w.kind == "tree" and w.rotary_mode)
                  else ("inline q theta=%g" % w.rope_theta if w.rotary_mode else "none"),
          "sm_scale": w.sm_scale}
-    if w.kind != "tree":
+    if w.kind == "ragged" and w.pad_mode:
+        c["valid_len_range"] = [int(np.min(w.valid_len)), int(np.max(w.valid_len))]
+    if w.kind == "paged":
         c["kv_chunk_range"] = [int(chunk_lengths(w).min()), int(chunk_lengths(w).max())]
         c["num_pages"] = w.num_pages
     return c
@@ -261,8 +281,8 @@ def main():
     w = make_extra(args.config) if args.config in EXTRA_NAMES else make_config(int(args.config))
     split = args.split
     if split is None:
-        split = 0 if args.config in EXTRA_NAMES else -1
-    if split >= 0 and w.kind == "tree":
+        split = 0 if args.config == "paged_decode" else -1
+    if split >= 0 and w.kind != "paged":
         split = -1
     launch_kw = {} if split < 0 else {"num_kv_splits": split}
     log("[bench] generated %s in %.1fs" % (w.name, time.perf_counter() - t_gen))

@@ -122,6 +122,32 @@ ra_status ra_paged_attn(const void* q, const int32_t* q_indptr, const void* page
                         float sm_scale, hipStream_t stream);
 
 /*
+ * Ragged prefill over contiguous K/V, optionally with padded batches.
+ * Sequence b's queries are q rows [q_indptr[b], q_indptr[b+1]) and its keys
+ * k/v rows [kv_indptr[b], kv_indptr[b+1]) (layouts as ra_tree_attn); query
+ * row t of the sequence sees key j under:
+ *   pad_mode 0: causal ? j < kv_len - qo_len + t + 1 : all keys
+ *               (_causal_mask on the "_kernel_common.py" page);
+ *   pad_mode 1: right padding (causal must be 0): t < valid_len[b] and
+ *               j < valid_len[b] (softmax_update_valid_length, same page);
+ *   pad_mode 2: left padding, causal (causal must be 1): the real queries are
+ *               [qo_len - valid, qo_len), the real keys [kv_len - valid,
+ *               kv_len), and j < kv_len - qo_len + t + 1
+ *               (softmax_update_causal_padded_left, same page).
+ * valid_len: [batch] int32 device array (NULL when pad_mode is 0); values are
+ * clamped to [0, qo_len] / [0, kv_len]. Rows with no visible key (padding
+ * rows) get out = 0, lse = -inf. No RoPE (rotate before calling).
+ * Errors: RA_EINVAL (NULL pointers, pad_mode not 0..2, pad_mode 1 with causal,
+ * pad_mode 2 without causal, sizes, sm_scale), RA_EUNSUPPORTED (head_dim,
+ * dtype), RA_EHIP (launch).
+ */
+ra_status ra_ragged_prefill(const void* q, const int32_t* q_indptr, const void* k, const void* v,
+                            const int32_t* kv_indptr, const int32_t* valid_len, int32_t pad_mode,
+                            int32_t causal, void* out, float* lse, int32_t batch,
+                            int32_t total_q, int32_t total_kv, int32_t h_q, int32_t h_kv,
+                            int32_t head_dim, ra_dtype dtype, float sm_scale, hipStream_t stream);
+
+/*
  * Split-KV form of ra_paged_attn, for few query rows over long KV (decode).
  * Same arguments and result as ra_paged_attn, plus:
  *   num_kv_splits   1..64: each work item's KV tiles are cut into this many

@@ -15,8 +15,9 @@ precision it follows them: the rotary embedding is evaluated in float32 and
 rounded to the storage dtype.
 
 Modules:
-  attention -- vectorised float64 oracle (tree_attn, paged_attn, rope, masks,
-               merge_states for split key sets)
+  attention -- vectorised float64 oracle (tree_attn, paged_attn,
+               ragged_prefill with padded masks, rope, masks, merge_states
+               for split key sets)
   scalar    -- pure-Python brute force for tiny inputs (ancestor sets from
                parent pointers rather than DFS intervals)
 """
@@ -27,7 +28,9 @@ from .attention import (  # noqa: F401
     causal_visible,
     kv_chunk_len,
     merge_states,
+    padded_visible,
     paged_attn,
+    ragged_prefill,
     rope,
     rope_exact,
     seq_offset,

@@ -337,3 +337,57 @@ def paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info, slidin
             vis = causal_visible(qi, L, qo_len, causal)
         _attend_sequence(qb, tok, qi, kb, vb, vis, h_q, h_kv, sm_scale, out, lse)
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# ragged prefill over contiguous K/V, with the padded-batch masks
+# ----------------------------------------------------------------------------
+
+def padded_visible(rows: np.ndarray, kv_len: int, qo_len: int, valid: int, pad_mode: int,
+                   causal: int) -> np.ndarray:
+    """Visibility [len(rows), kv_len] for query rows of one sequence.
+
+    pad_mode 0: the causal test (_causal_mask, "_kernel_common.py" page).
+    pad_mode 1: right padding, macro softmax_update_valid_length on the same
+      page: row < qo_len, row < valid and col < valid.
+    pad_mode 2: left padding with causal alignment, macro
+      softmax_update_causal_padded_left: row in [qo_len - valid, qo_len),
+      col in [kv_len - valid, kv_len - qo_len + row + 1)."""
+    rows = np.asarray(rows)
+    col = np.arange(kv_len)[None, :]
+    r = rows[:, None]
+    if pad_mode == 0:
+        return causal_visible(rows, kv_len, qo_len, causal)
+    if pad_mode == 1:
+        return (r < qo_len) & (r < valid) & (col < valid)
+    if pad_mode == 2:
+        pad_q, pad_kv = qo_len - valid, kv_len - valid
+        return (r < qo_len) & (r >= pad_q) & (col >= pad_kv) & (col < kv_len - qo_len + r + 1)
+    raise ValueError(pad_mode)
+
+
+def ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len, pad_mode: int, causal: int,
+                   sm_scale: float, rows: Optional[np.ndarray] = None):
+    """Ragged prefill: sequence b's queries q[q_indptr[b]:q_indptr[b+1]]
+    attend to k/v[kv_indptr[b]:kv_indptr[b+1]] under padded_visible.
+    Returns (out [total_q, h_q, d], lse [total_q, h_q]) float64."""
+    total_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    out = np.full((total_q, h_q, d), np.nan)
+    lse = np.full((total_q, h_q), np.nan)
+    q_indptr = np.asarray(q_indptr)
+    kv_indptr = np.asarray(kv_indptr)
+    for b in range(len(q_indptr) - 1):
+        qi = _select_tokens(q_indptr, rows, b)
+        if len(qi) == 0:
+            continue
+        q0 = int(q_indptr[b])
+        qo_len = int(q_indptr[b + 1]) - q0
+        k0, k1 = int(kv_indptr[b]), int(kv_indptr[b + 1])
+        L = k1 - k0
+        valid = 0 if valid_len is None else int(np.asarray(valid_len)[b])
+        vis = padded_visible(qi, L, qo_len, valid, pad_mode, causal)
+        tok = q0 + qi
+        _attend_sequence(_f64(q[tok]), tok, qi, _f64(k[k0:k1]), _f64(v[k0:k1]), vis, h_q, h_kv,
+                         sm_scale, out, lse)
+    return out, lse

@@ -42,6 +42,9 @@ def say(msg: str):
 
 
 def run_oracle(w, rows=None):
+    if w.kind == "ragged":
+        return oracle.ragged_prefill(w.q, w.q_indptr, w.k, w.v, w.kv_indptr, w.valid_len,
+                                     w.pad_mode, w.causal, w.sm_scale, rows=rows)
     if w.kind == "tree":
         return oracle.tree_attn(w.q, w.q_indptr, w.k, w.v, w.kv_indptr, w.q_rope_position,
                                 w.mn_indptr, w.tree_mask, w.rotary_mode, w.rope_scale,

@@ -10,7 +10,7 @@ import torch
 import bench
 import oracle
 from tests.parity import out_tolerance
-from workloads import make_config, make_custom_paged, make_custom_tree
+from workloads import make_config, make_custom_paged, make_custom_ragged, make_custom_tree
 
 
 def _count_with_oracle(w):
@@ -22,7 +22,10 @@ def _count_with_oracle(w):
         if qo == 0:
             continue
         rows = np.arange(qo)
-        if w.kind == "tree":
+        if w.kind == "ragged":
+            vis = oracle.padded_visible(rows, int(L[b]), qo, int(w.valid_len[b]) if w.pad_mode else 0,
+                                        w.pad_mode, w.causal)
+        elif w.kind == "tree":
             vis = oracle.tree_visible(w.tree_mask[int(w.mn_indptr[b]):int(w.mn_indptr[b + 1])], rows, int(L[b]), qo)
         elif w.tree_order is not None:
             t = w.tree_order[int(w.tree_order_indptr[b]):int(w.tree_order_indptr[b + 1])]
@@ -43,6 +46,11 @@ def test_visible_pairs_tree_and_causal():
         make_custom_paged(4, [20, 9], [200, 77], h_q=4, h_kv=2, d=64, dtype="bf16", causal=1,
                           sliding=([136, 37], [4, 0])),
         make_custom_paged(5, [6, 11], [26, 14], h_q=4, h_kv=2, d=64, dtype="f16", causal=0, tree=True),
+        make_custom_ragged(6, [9, 12, 5], [9, 12, 7], h_q=4, h_kv=2, d=16, dtype="f16", causal=0,
+                           pad_mode=1, valid_lens=[6, 15, 0]),
+        make_custom_ragged(7, [8, 11, 4], [13, 11, 6], h_q=4, h_kv=2, d=16, dtype="f16", causal=1,
+                           pad_mode=2, valid_lens=[5, 11, 0]),
+        make_custom_ragged(8, [8, 20], [13, 20], h_q=4, h_kv=2, d=16, dtype="f16", causal=1),
     ]
     for w in cases:
         assert bench.visible_pairs(w) == _count_with_oracle(w), w.name

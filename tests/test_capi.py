@@ -159,6 +159,20 @@ def test_merge_rejects(lib):
     assert lib.ra_merge_states(P, P, 2, 0, 128, 1, P, P, None) == ra.RA_OK
 
 
+def test_ragged_prefill_rejects(lib):
+    P = ctypes.c_void_p(0x1000)
+    def call(valid=P, pad=0, causal=1, batch=1, total_q=4, d=128, kv=P):
+        return lib.ra_ragged_prefill(P, P, P, P, kv, valid, pad, causal, P, P, batch, total_q, 8, 8, 2,
+                                     d, 1, 0.1, None)
+    assert call(pad=3) == ra.RA_EINVAL
+    assert call(pad=1, causal=1) == ra.RA_EINVAL       # right padding is not causal
+    assert call(pad=2, causal=0) == ra.RA_EINVAL       # left padding is causal
+    assert call(pad=1, causal=0, valid=None) == ra.RA_EINVAL
+    assert call(kv=None) == ra.RA_EINVAL
+    assert call(d=80) == ra.RA_EUNSUPPORTED
+    assert call(batch=0, total_q=0) == ra.RA_OK
+
+
 def test_append_rejects(lib):
     P = ctypes.c_void_p(0x1000)
     st = lib.ra_paged_kv_append(P, P, P, P, None, P, P, P, 0, 5, 4, 4, 16, 2, 128, 1, 1.0, 1e4, None)

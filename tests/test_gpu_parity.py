@@ -248,3 +248,38 @@ def test_paged_decode_full_size_split():
         out, lse = di.launch() if splits is None else di.launch(num_kv_splits=splits)
         torch.cuda.synchronize()
         compare(out, lse, ref_out, ref_lse, label="paged_decode/%s" % splits)
+
+
+# ---------------------------------------------------------------------------
+# ragged prefill over contiguous K/V, padded batches
+# ---------------------------------------------------------------------------
+
+RAGGED_CASES = {
+    "causal_bf16_d128": dict(seed=60, qo=[300, 1, 0, 129], kv=[700, 1, 5, 129], h_q=32, h_kv=8,
+                             d=128, dtype="bf16", causal=1),
+    "full_f16_d64": dict(seed=61, qo=[77, 200], kv=[50, 333], h_q=8, h_kv=8, d=64, dtype="f16",
+                         causal=0),
+    "right_pad_bf16": dict(seed=62, qo=[256, 256, 256, 100], kv=[256, 256, 256, 300], h_q=16, h_kv=4,
+                           d=128, dtype="bf16", causal=0, pad_mode=1, valid_lens=[100, 256, 0, 400]),
+    "right_pad_f16_d64": dict(seed=63, qo=[130, 70], kv=[130, 90], h_q=8, h_kv=2, d=64, dtype="f16",
+                              causal=0, pad_mode=1, valid_lens=[65, 1]),
+    "left_pad_causal_bf16": dict(seed=64, qo=[256, 256, 256, 64], kv=[256, 256, 300, 64], h_q=16,
+                                 h_kv=4, d=128, dtype="bf16", causal=1, pad_mode=2,
+                                 valid_lens=[100, 256, 200, 0]),
+    "left_pad_causal_f16_d64": dict(seed=65, qo=[190, 33], kv=[190, 40], h_q=8, h_kv=1, d=64,
+                                    dtype="f16", causal=1, pad_mode=2, valid_lens=[129, 500]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED_CASES))
+def test_ragged_prefill_padded(case):
+    from workloads import make_custom_ragged
+    c = dict(RAGGED_CASES[case])
+    w = make_custom_ragged(c.pop("seed"), c.pop("qo"), c.pop("kv"), **c)
+    _check(w, "ragged %s" % case)
+
+
+def test_ragged_left_padded_workload_sampled():
+    from workloads import make_extra
+    w = make_extra("ragged_left_padded")
+    _check(w, w.name, rows=sample_rows(w, per_seq=24, seed=3))

@@ -450,3 +450,59 @@ def test_merge_two_equal_halves_closed_form():
     o, l = oracle.merge_states(po, pl)
     np.testing.assert_allclose(l, [1.5], atol=1e-15)
     np.testing.assert_allclose(o, [[2.0, 1.0]], atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# padded-batch masks (ragged prefill over contiguous K/V)
+# ---------------------------------------------------------------------------
+
+def _ragged(seed, qo, kv, h_q=4, h_kv=2, d=16):
+    rng = np.random.default_rng(seed)
+    q = torch.from_numpy(rng.standard_normal((sum(qo), h_q, d))).to(torch.float16)
+    k = torch.from_numpy(rng.standard_normal((sum(kv), h_kv, d))).to(torch.float16)
+    v = torch.from_numpy(rng.standard_normal((sum(kv), h_kv, d))).to(torch.float16)
+    return q, np.concatenate([[0], np.cumsum(qo)]), k, v, np.concatenate([[0], np.cumsum(kv)])
+
+
+def test_right_padding_equals_attention_on_the_valid_prefix():
+    qo, kv, valid = [9, 12, 5], [9, 12, 7], [6, 12, 0]
+    q, qi, k, v, ki = _ragged(50, qo, kv)
+    out, lse = oracle.ragged_prefill(q, qi, k, v, ki, np.array(valid), 1, 0, 0.4)
+    for b in range(3):
+        n = valid[b]
+        if n:
+            ro, rl = oracle.ragged_prefill(q[qi[b]:qi[b] + n], np.array([0, n]), k[ki[b]:ki[b] + n],
+                                           v[ki[b]:ki[b] + n], np.array([0, n]), None, 0, 0, 0.4)
+            np.testing.assert_allclose(out[qi[b]:qi[b] + n], ro, atol=1e-12)
+            np.testing.assert_allclose(lse[qi[b]:qi[b] + n], rl, atol=1e-12)
+        # padding rows see nothing
+        assert np.all(np.isneginf(lse[qi[b] + n:qi[b + 1]])) and np.all(out[qi[b] + n:qi[b + 1]] == 0)
+
+
+def test_left_padding_equals_causal_attention_on_the_valid_suffix():
+    qo, kv, valid = [8, 11, 4], [13, 11, 6], [5, 11, 0]
+    q, qi, k, v, ki = _ragged(51, qo, kv)
+    out, lse = oracle.ragged_prefill(q, qi, k, v, ki, np.array(valid), 2, 1, 0.4)
+    for b in range(3):
+        n = valid[b]
+        pq, pk = qo[b] - n, kv[b] - n
+        if n:
+            sq, sk = slice(qi[b] + pq, qi[b + 1]), slice(ki[b] + pk, ki[b + 1])
+            ro, rl = oracle.ragged_prefill(q[sq], np.array([0, n]), k[sk], v[sk], np.array([0, n]),
+                                           None, 0, 1, 0.4)
+            np.testing.assert_allclose(out[sq], ro, atol=1e-12)
+            np.testing.assert_allclose(lse[sq], rl, atol=1e-12)
+        assert np.all(np.isneginf(lse[qi[b]:qi[b] + pq])) and np.all(out[qi[b]:qi[b] + pq] == 0)
+
+
+def test_plain_ragged_prefill_matches_paged_causal():
+    """pad_mode 0 over contiguous K/V equals the paged causal path on the
+    same rows (two independent gathers of the same definition)."""
+    w = make_custom_paged(52, [7, 20], [30, 20], h_q=4, h_kv=2, d=16, dtype="f16", causal=1)
+    po, pl = oracle.paged_attn(w.q, w.q_indptr, pages_from_logical(w), w.page_indptr, w.page_values,
+                               w.length_info, 0, 1, w.sm_scale, w.dtype)
+    k = torch.cat([w.k_store[int(w.kv_store_indptr[b]):int(w.kv_store_indptr[b + 1])] for b in range(2)])
+    v = torch.cat([w.v_store[int(w.kv_store_indptr[b]):int(w.kv_store_indptr[b + 1])] for b in range(2)])
+    ro, rl = oracle.ragged_prefill(w.q, w.q_indptr, k, v, w.kv_store_indptr, None, 0, 1, w.sm_scale)
+    np.testing.assert_allclose(ro, po, atol=1e-12)
+    np.testing.assert_allclose(rl, pl, atol=1e-12)

@@ -15,6 +15,7 @@ from .generators import (  # noqa: F401
     dfs_intervals,
     make_config,
     make_custom_paged,
+    make_custom_ragged,
     make_custom_tree,
     make_extra,
     pages_from_logical,

@@ -52,6 +52,11 @@ class DeviceInputs:
             self.kv_indptr = _i32(w.kv_indptr, d)
             self.mn_indptr = _i32(w.mn_indptr, d)
             self.tree_mask = _i32(w.tree_mask.reshape(-1, 2), d)
+        elif w.kind == "ragged":
+            self.k = w.k.to(d)
+            self.v = w.v.to(d)
+            self.kv_indptr = _i32(w.kv_indptr, d)
+            self.valid_len = _i32(w.valid_len, d)
         else:
             self.pages = gpu_pages(w, d)
             self.page_indptr = _i32(w.page_indptr, d)
@@ -67,7 +72,7 @@ class DeviceInputs:
         import attention_ragged_gqa_amd as ra
         w = self.w
         if num_kv_splits is not None:
-            if w.kind == "tree":
+            if w.kind != "paged":
                 raise ValueError("split-KV is a paged entry point")
             if getattr(self, "workspace", None) is None:
                 n = ra.ra_paged_attn_split_workspace(w.total_q, w.h_q, w.d, 64)
@@ -80,6 +85,11 @@ class DeviceInputs:
                 causal=w.causal, out=self.out, lse=self.lse, rotary_mode=w.rotary_mode,
                 rope_scale=w.rope_scale, rope_theta=w.rope_theta, sm_scale=w.sm_scale,
                 num_kv_splits=num_kv_splits, workspace=self.workspace, stream=stream)
+        if w.kind == "ragged":
+            return ra.ra_ragged_prefill(self.q, self.q_indptr, self.k, self.v, self.kv_indptr,
+                                        valid_len=self.valid_len, pad_mode=w.pad_mode,
+                                        causal=w.causal, out=self.out, lse=self.lse,
+                                        sm_scale=w.sm_scale, stream=stream)
         if w.kind == "tree":
             return ra.ra_tree_attn(self.q, self.q_indptr, self.k, self.v, self.kv_indptr,
                                    self.q_rope_position, self.mn_indptr, self.tree_mask,

@@ -115,7 +115,7 @@ class Workload:
     """One batch of attention inputs (CPU tensors / numpy arrays)."""
 
     name: str
-    kind: str                      # "tree" (contiguous KV) or "paged"
+    kind: str                      # "tree" / "ragged" (contiguous KV) or "paged"
     dtype: str                     # "f16" or "bf16"
     batch: int
     h_q: int
@@ -154,6 +154,9 @@ class Workload:
     # Position at which each stored K token is rotated before caching (the
     # "normal" RoPE mode of the KV cache); None when K is stored unrotated.
     store_rope_position: Optional[np.ndarray] = None
+    # ragged prefill over contiguous K/V (kind "ragged"): padded-batch masks
+    pad_mode: int = 0
+    valid_len: Optional[np.ndarray] = None          # [b]
 
     @property
     def total_q(self) -> int:
@@ -325,15 +328,45 @@ def make_custom_paged(seed: int, qo_lens, stored_lens, h_q: int, h_kv: int, d: i
     return w
 
 
+def make_custom_ragged(seed: int, qo_lens, kv_lens, h_q: int, h_kv: int, d: int, dtype: str,
+                       causal: int = 1, pad_mode: int = 0, valid_lens=None,
+                       sm_scale: Optional[float] = None, name: str = "custom_ragged",
+                       rng: Optional[np.random.Generator] = None) -> Workload:
+    """Ragged prefill over contiguous K/V: sequence b has qo_lens[b] queries
+    and kv_lens[b] keys (q_indptr / kv_indptr); pad_mode / valid_lens select
+    the padded-batch masks (1: right padding, 2: left padding, causal)."""
+    rng = _rng(seed) if rng is None else rng
+    qo = [int(x) for x in qo_lens]
+    kv = [int(x) for x in kv_lens]
+    q_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    kv_indptr = np.concatenate([[0], np.cumsum(kv)]).astype(np.int32)
+    q = _normal(rng, (int(q_indptr[-1]), h_q, d), dtype)
+    k = _normal(rng, (int(kv_indptr[-1]), h_kv, d), dtype)
+    v = _normal(rng, (int(kv_indptr[-1]), h_kv, d), dtype)
+    return Workload(name=name, kind="ragged", dtype=dtype, batch=len(qo), h_q=h_q, h_kv=h_kv, d=d,
+                    sm_scale=(1.0 / math.sqrt(d)) if sm_scale is None else sm_scale,
+                    q=q, q_indptr=q_indptr, k=k, v=v, kv_indptr=kv_indptr, causal=int(causal),
+                    pad_mode=int(pad_mode),
+                    valid_len=None if valid_lens is None else np.asarray(valid_lens, np.int32))
+
+
 # Workloads beyond the five configurations, for entry points adjacent to
-# the main path (split-KV decode).
-EXTRA_NAMES = ("paged_decode",)
+# the main path (split-KV decode, padded batches).
+EXTRA_NAMES = ("paged_decode", "ragged_left_padded")
 
 
 def make_extra(name: str, seed: Optional[int] = None) -> Workload:
     """paged_decode: 16 sequences decoding one token each over 8K-24K cached
     tokens (K rotated when cached, pages permuted), h_q 32 / h_kv 8, d 128,
     bf16, causal. Seed 2000."""
+    if name == "ragged_left_padded":
+        # 8 prompts left-padded to 2048 tokens (valid 512..2048), causal
+        # prefill over their own keys, h 32/8, d 128, bf16. Seed 2001.
+        seed = 2001 if seed is None else seed
+        rng = _rng(seed)
+        valid = rng.integers(512, 2049, size=8)
+        return make_custom_ragged(seed, [2048] * 8, [2048] * 8, h_q=32, h_kv=8, d=128, dtype="bf16",
+                                  causal=1, pad_mode=2, valid_lens=valid, name=name, rng=rng)
     if name != "paged_decode":
         raise KeyError(name)
     seed = 2000 if seed is None else seed

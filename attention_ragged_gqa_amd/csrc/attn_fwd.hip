@@ -339,6 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int lim_m = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
   int lo_m = 0;
   int kv_hi = kv_len;
+  int kv_lo = 0;   // first key any row of the tile can see
   const int t_last = min((row0 + kBM - 1) / g, qo_len - 1);
   if (causal) kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
   if (pad_mode == 1) {          // right padding: rows and keys below valid_len
@@ -349,6 +350,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     const int vq = min(max(valid_m, 0), qo_len), vk = min(max(valid_m, 0), kv_len);
     lo_m = kv_len - vk;
     if (t < qo_len - vq) lim_m = 0;
+    kv_lo = kv_len - vk;
+    if (t_last < qo_len - vq) kv_hi = 0;   // the whole tile is padding
   }
   const int lim = lim_m, lo = lo_m;
   int lim_lo = causal ? min(kv_len, kv_len - qo_len + t_lo + 1) : kv_len;
@@ -371,12 +374,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     lo_min = __builtin_amdgcn_readfirstlane(lmin);
     lo_max = __builtin_amdgcn_readfirstlane(lmax);
   }
-  const int n_tiles_all = kv_hi > 0 ? (kv_hi + kBN - 1) / kBN : 0;
+  // Paged sliding window: keys past the sink sit at storage offset j + delta.
+  // The tile grid is shifted back by kshift = delta mod 16 keys, so that every
+  // 16-row block past the sink is exactly one page (the keys j < 0 this adds
+  // to the first tile are masked).
+  const int delta = (LAYOUT == kPaged && sliding_) ? win_off - sink : 0;
+  const int kshift = delta & 15;
+  // KV tiles the item needs: [kv_lo, kv_hi) on that grid
+  const int tile0 = (kv_lo + kshift) / kBN;
+  const int n_tiles_all = kv_hi > kv_lo ? (kv_hi + kshift + kBN - 1) / kBN - tile0 : 0;
   // split-KV: this item's contiguous range of those tiles
   const int tile_lo = (splits > 1) ? split * n_tiles_all / splits : 0;
   const int tile_hi = (splits > 1) ? (split + 1) * n_tiles_all / splits : n_tiles_all;
   const int n_tiles = tile_hi - tile_lo;   // tiles this workgroup processes
-  const int jbase = tile_lo * kBN;         // first key of the range
+  const int jbase = (tile0 + tile_lo) * kBN - kshift;   // first key of the range
 
   // enter index of this row's tree node (selected after the prologue)
   const int c_node = t + tree_len - qo_len;
@@ -388,44 +399,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const int pc = lane % CH;
   const int lrow = lane / CH;
   auto tile_row = [&](int i) __attribute__((always_inline)) { return 16 * w + RPL * i + lrow; };
-  const int delta = sliding_ ? win_off - sink : 0;   // window: storage offset - position
-  // Page numbers are wave-uniform scalars: the 16 rows [B, B + 16) a wave
-  // loads (B = j0 + 16w, 16-aligned) touch at most three pages: the page of
-  // sink positions (storage offset = position) and the two pages that the
-  // window offsets starting at max(B, sink) + delta can straddle.
-  // The loaded page numbers are only inspected when the next tile is issued
-  // (after the barrier): validating them right after the load would make the
-  // compiler wait for all outstanding loads, including the K/V prefetch.
-  struct PageSet {
-    int ia, ib, ic;   // page_values indices (wave-uniform)
-    int va, vb, vc;   // raw page numbers loaded from them
-    int offb;         // first window storage offset of the block
+  // Page of the wave's 16-row block [B, B + 16) of a tile, B = j0 + 16w.
+  // Past the sink such a block is one whole page (storage offsets
+  // B + delta, a multiple of 16 on the shifted grid). The page number is
+  // loaded a tile ahead and only read (v_readfirstlane) when the block is
+  // issued; out-of-range indices read 0 and are rejected there.
+  const __amdgpu_buffer_rsrc_t page_rsrc = make_rsrc(page_values_, 4L * nnz_pages_);
+  auto fetch_page = [&](int j0) __attribute__((always_inline)) -> int {
+    if constexpr (LAYOUT == kPaged) return load_i32(page_rsrc, page_base + ((j0 + 16 * w + delta) >> 4));
+    else return 0;
   };
-  auto load_page = [&](int pidx) __attribute__((always_inline)) -> int {
-    return page_values_[min(max(pidx, 0), nnz_pages_ - 1)];   // in bounds; checked at use
-  };
-  auto fetch_pages = [&](int j0) __attribute__((always_inline)) -> PageSet {
-    PageSet ps{-1, -1, -1, 0, 0, 0, 0};
-    if constexpr (LAYOUT == kPaged) {
-      const int B = j0 + 16 * w;
-      ps.offb = (sliding_ ? max(B, sink) : B) + delta;
-      ps.ia = (sliding_ && B < sink) ? page_base + (B >> 4) : -1;
-      ps.ib = page_base + (ps.offb >> 4);
-      ps.ic = (ps.offb & 15) ? ps.ib + 1 : -1;
-      ps.va = load_page(ps.ia);
-      ps.vb = load_page(ps.ib);
-      ps.vc = load_page(ps.ic);
-    }
-    return ps;
-  };
-  auto page_ok = [&](int idx, int val) __attribute__((always_inline)) -> bool {
-    return idx >= page_base && idx < page_end &&
-           static_cast<unsigned>(val) < static_cast<unsigned>(num_pages_);
-  };
-  PageSet pages_next{-1, -1, -1, 0, 0, 0, 0};   // pages of the next tile to load
-  // byte address of the head row of chunk position kidx (K: which = 0, V: 1)
-  const size_t kv_stride = static_cast<size_t>(h_kv_) * RB;              // contiguous: per token
-  const size_t page_stride = static_cast<size_t>(2) * h_kv_ * 16 * RB;   // paged: per page
+  int page_next = 0;   // page of this wave's block of the next tile to issue
+  const size_t kv_stride = static_cast<size_t>(h_kv_) * RB;           // contiguous: per token
+  const uint32_t page_stride = static_cast<uint32_t>(2 * h_kv_ * 16 * RB);   // paged: per page
   const char* kv_head_k;
   const char* kv_head_v;
   if constexpr (LAYOUT == kContiguous) {
@@ -435,23 +421,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     kv_head_k = reinterpret_cast<const char*>(pages_) + static_cast<size_t>(kvh) * 16 * RB;
     kv_head_v = kv_head_k + static_cast<size_t>(h_kv_) * 16 * RB;
   }
-  auto row_addr = [&](int kidx, int which, PageSet ps) __attribute__((always_inline)) -> const char* {
-    const char* base = which ? kv_head_v : kv_head_k;
-    if (kidx >= kv_len) return nullptr;
+  const size_t v_minus_k = static_cast<size_t>(kv_head_v - kv_head_k);
+  // Blocks that take the whole-block path: B in [fast_lo, fast_hi - 16] and,
+  // when paged, a page number below num_pages. Everything else (sink rows,
+  // keys j < 0, the chunk's ragged end, rows of pages outside the sequence's
+  // range or past the cache) goes row by row.
+  int fast_lo = 0, fast_hi;
+  if constexpr (LAYOUT == kContiguous) {
+    fast_hi = min(kv_len, total_kv_ - kv_base);
+  } else {
+    if (sliding_) fast_lo = max(sink, 0);
+    fast_hi = min(kv_len, (page_end - page_base) * 16 - delta);
+  }
+  auto block_fast = [&](int B, int pg) __attribute__((always_inline)) -> bool {
+    const bool rows = B >= fast_lo && B + 16 <= fast_hi;
+    if constexpr (LAYOUT == kPaged) return rows && static_cast<unsigned>(pg) < static_cast<unsigned>(num_pages_);
+    else return rows;
+  };
+  auto block_base = [&](int B, int pg) __attribute__((always_inline)) -> const char* {
+    if constexpr (LAYOUT == kContiguous) return kv_head_k + static_cast<size_t>(B) * kv_stride;
+    else return kv_head_k + static_cast<size_t>(static_cast<uint32_t>(pg)) * page_stride;
+  };
+  // Per-row K source of chunk position kidx (V: + v_minus_k), or null for a
+  // row outside the chunk or with an invalid page. page: the page number
+  // loaded for the row (row_page_index below).
+  auto row_page_index = [&](int kidx) __attribute__((always_inline)) -> int {
+    const int off = (sliding_ && kidx < sink) ? kidx : kidx + delta;
+    return page_base + (off >> 4);
+  };
+  auto row_src = [&](int kidx, int page) __attribute__((always_inline)) -> const char* {
+    if (kidx < 0 || kidx >= kv_len) return nullptr;
     if constexpr (LAYOUT == kContiguous) {
       const int r = kv_base + kidx;
       if (r < 0 || r >= total_kv_) return nullptr;
-      return base + static_cast<size_t>(kidx) * kv_stride;
+      return kv_head_k + static_cast<size_t>(kidx) * kv_stride;
     } else {
-      const bool in_sink = sliding_ && kidx < sink;
-      const int off = in_sink ? kidx : kidx + delta;
-      // values, not an indexed struct (which the compiler would put in memory)
-      const int ia = ps.ia, ib = ps.ib, ic = ps.ic, va = ps.va, vb = ps.vb, vc = ps.vc;
-      const bool second = (off >> 4) != (ps.offb >> 4);
-      const int idx = in_sink ? ia : (second ? ic : ib);
-      const int page = in_sink ? va : (second ? vc : vb);
-      if (!page_ok(idx, page)) return nullptr;
-      return base + static_cast<size_t>(page) * page_stride + (off & 15) * RB;
+      const int off = (sliding_ && kidx < sink) ? kidx : kidx + delta;
+      const int idx = page_base + (off >> 4);
+      if (off < 0 || idx >= page_end || static_cast<unsigned>(page) >= static_cast<unsigned>(num_pages_))
+        return nullptr;
+      return kv_head_k + static_cast<size_t>(static_cast<uint32_t>(page)) * page_stride + (off & 15) * RB;
     }
   };
 
@@ -464,89 +473,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     const int r = tile_row(i);
     return static_cast<uint32_t>(RPL * i + lrow) * mem_rs + 16 * (pc ^ (v ? VSWZ(r) : KSWZ(r)));
   };
-  const size_t v_minus_k = static_cast<size_t>(kv_head_v - kv_head_k);
   auto zero_row = [&](char* dst) __attribute__((always_inline)) {
     *reinterpret_cast<u32x4*>(dst + 16 * lane) = u32x4{0, 0, 0, 0};
   };
-  // The wave's 16-row block [B, B + 16) of tile j0 as at most two runs of
-  // rows with a common base: rows rl < split use base_a, the others base_b
-  // (paged: the block's storage offsets straddle two pages; contiguous:
-  // split = 16). Rows rl >= nvalid, or in a page that fails validation, are
-  // zero-filled. Returns false for blocks that need per-row addressing
-  // (sink positions of a sliding window).
-  struct Block {
-    const char* base_a;
-    const char* base_b;
-    int split, nvalid;
-    bool ok_a, ok_b;
-  };
-  auto block_of = [&](int j0, PageSet ps, Block& bl) __attribute__((always_inline)) -> bool {
-    const int B = j0 + 16 * w;
-    if constexpr (LAYOUT == kContiguous) {
-      bl.base_a = kv_head_k + static_cast<size_t>(B) * kv_stride;
-      bl.base_b = bl.base_a;
-      bl.split = 16;
-      bl.nvalid = min(kv_len, total_kv_ - kv_base) - B;
-      bl.ok_a = bl.ok_b = true;
-      return true;
-    } else {
-      if (sliding_ && B < sink) return false;
-      const int O = B + delta;                      // storage offset of row 0
-      const int intra = O & 15;
-      const int ia = ps.ib, ib = ps.ic;             // page_values indices
-      const int pa = __builtin_amdgcn_readfirstlane(ps.vb);
-      const int pb = __builtin_amdgcn_readfirstlane(ps.vc);
-      bl.ok_a = page_ok(ia, pa);
-      bl.ok_b = intra == 0 || page_ok(ib, pb);
-      bl.base_a = kv_head_k + static_cast<size_t>(bl.ok_a ? pa : 0) * page_stride + intra * RB;
-      bl.base_b = kv_head_k + static_cast<size_t>(bl.ok_b ? pb : 0) * page_stride - (16 - intra) * RB;
-      bl.split = 16 - intra;
-      bl.nvalid = kv_len - B;
-      return true;
-    }
+  // Row pages of the slow path: all loads first, then one wait, here. (A
+  // load left pending past the slow path would make the tile loop wait for
+  // it, and with it for the next tile's loads, before every tile.)
+  auto row_pages = [&](int j0, int (&pg)[LOADS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      pg[i] = LAYOUT == kPaged ? load_i32(page_rsrc, row_page_index(j0 + tile_row(i))) : 0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) pin(pg[i]);
   };
 
   auto issue_tile = [&](int j0, char* stage) __attribute__((always_inline)) {
-    Block bl;
-    if (block_of(j0, pages_next, bl)) {
-      const bool whole = bl.nvalid >= 16 && bl.ok_a && bl.split == 16;   // uniform
+    const int B = j0 + 16 * w;
+    const int pg = __builtin_amdgcn_readfirstlane(page_next);
+    if (block_fast(B, pg)) {
+      const char* base = block_base(B, pg);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         char* dst_k = stage + (16 * w + RPL * i) * RB;          // wave-uniform
-        const uint32_t ok_ = lane_off(i, false), ov = lane_off(i, true);
-        if (whole) {
-          if constexpr (!ROPE_K) dma16s(bl.base_a, ok_, dst_k);
-          dma16s(bl.base_a + v_minus_k, ov, dst_k + TILE);
-        } else {
-          const int rl = RPL * i + lrow;
-          const bool in_a = rl < bl.split;
-          const bool valid = rl < bl.nvalid && (in_a ? bl.ok_a : bl.ok_b);
-          if (valid && in_a) {
-            if constexpr (!ROPE_K) dma16s(bl.base_a, ok_, dst_k);
-            dma16s(bl.base_a + v_minus_k, ov, dst_k + TILE);
-          }
-          if (valid && !in_a) {
-            if constexpr (!ROPE_K) dma16s(bl.base_b, ok_, dst_k);
-            dma16s(bl.base_b + v_minus_k, ov, dst_k + TILE);
-          }
-          if (!valid) {
-            // rows past the chunk: zeros, so masked products stay finite
-            if constexpr (!ROPE_K) zero_row(dst_k);
-            zero_row(dst_k + TILE);
-          }
-        }
+        if constexpr (!ROPE_K) dma16s(base, lane_off(i, false), dst_k);
+        dma16s(base + v_minus_k, lane_off(i, true), dst_k + TILE);
       }
     } else {
-      // per-row addressing (blocks holding sink positions)
+      int rp[LOADS];
+      row_pages(j0, rp);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int r = tile_row(i);
         char* dst_k = stage + (16 * w + RPL * i) * RB;
-        const char* src = row_addr(j0 + r, 0, pages_next);
+        const char* src = row_src(j0 + r, rp[i]);
         if (src) {
           if constexpr (!ROPE_K) dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
           dma16(src + v_minus_k + 16 * (pc ^ VSWZ(r)), dst_k + TILE);
         } else {
+          // rows outside the chunk: zeros, so masked products stay finite
           if constexpr (!ROPE_K) zero_row(dst_k);
           zero_row(dst_k + TILE);
         }
@@ -573,21 +537,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   };
   auto load_k_regs = [&](int j0) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
-      Block bl;
-      if (block_of(j0, pages_next, bl)) {
+      const int B = j0 + 16 * w;
+      const int pg = __builtin_amdgcn_readfirstlane(page_next);
+      if (block_fast(B, pg)) {
+        const char* base = block_base(B, pg);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int rl = RPL * i + lrow;
-          const bool in_a = rl < bl.split;
-          const bool valid = rl < bl.nvalid && (in_a ? bl.ok_a : bl.ok_b);
-          const char* base = in_a ? bl.base_a : bl.base_b;
-          kreg[i] = valid ? *reinterpret_cast<const u32x4*>(base + lane_off(i, false)) : u32x4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < LOADS; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(base + lane_off(i, false));
       } else {
+        int rp[LOADS];
+        row_pages(j0, rp);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
           const int r = tile_row(i);
-          const char* src = row_addr(j0 + r, 0, pages_next);
+          const char* src = row_src(j0 + r, rp[i]);
           kreg[i] = src ? *reinterpret_cast<const u32x4*>(src + 16 * (pc ^ KSWZ(r))) : u32x4{0, 0, 0, 0};
         }
       }
@@ -679,16 +641,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     if (n_tiles > 0) {
       issue_tile(jbase, smem);                             // V (and K) straight into stage 0
       load_k_regs(jbase);
-      if (n_tiles > 1) pages_next = fetch_pages(jbase + kBN);   // pages of the second tile
+      if (n_tiles > 1) page_next = fetch_page(jbase + kBN);   // page of the second tile
     }
   };
   if constexpr (LAYOUT == kPaged) {
-    if (n_tiles > 0) pages_next = fetch_pages(jbase);
-    // one wait for the page numbers here; otherwise each row of the tile
-    // would wait again, behind the loads issued for the rows before it
-    pin(pages_next.va);
-    pin(pages_next.vb);
-    pin(pages_next.vc);
+    if (n_tiles > 0) page_next = fetch_page(jbase);
+    // one wait for the page number here, before the tile-0 loads go out
+    pin(page_next);
     issue_first_tile();
   }
 
@@ -836,14 +795,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         }
       }
     }
-    f32x16 sacc[2];
+    // The two 32-key blocks alternate, so consecutive MFMAs are independent,
+    // and every K fragment is read kAhead MFMAs before its use: the LDS
+    // latency hides behind the MFMAs instead of stalling each one.
+    constexpr int NF = 2 * (D / 16);
+    constexpr int kAhead = 4;
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    u32x4 kf[NF];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int t = 0; t < NF; ++t)
+      kf[t] = *reinterpret_cast<const u32x4*>(smem + (t & 1) * 32 * RB + koff[t >> 1]);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        sacc[kb] = mma32<BF>(*reinterpret_cast<const u32x4*>(smem + kb * 32 * RB + koff[s]), qf[s], sacc[kb]);
+    for (int t = 0; t < NF; ++t) sacc[t & 1] = mma32<BF>(kf[t], qf[t >> 1], sacc[t & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
+#pragma unroll
+    for (int t = 0; t < NF - kAhead; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     if (masked) {
       if constexpr (MASK == kMaskTree) {
 #pragma unroll
@@ -854,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       } else {
         // key j0 + 4hh + c(kb, r) is visible iff lo - j0 - 4hh <= c < lim - j0 - 4hh
         const int rel = lim - j0 - 4 * hh;
-        if (lo_max == 0) {   // uniform: no lower bound (always, without left padding)
+        if (lo_max == 0 && j0 >= 0) {   // uniform: no lower bound (no left padding, no keys j < 0)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -938,7 +908,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       load_k_regs(j0 + kBN);
       if constexpr (MASK == kMaskTree)
         win_iv = load_i32x2(tree_rsrc, tree_base + j0 + kBN + (tid & (kBN - 1)) - tree_start);
-      if (it + 2 < n_tiles) pages_next = fetch_pages(j0 + 2 * kBN);
+      if (it + 2 < n_tiles) page_next = fetch_page(j0 + 2 * kBN);
     }
     // tile class for this wave: 0 skip, 1 full, 2 partial
     int cls;

@@ -762,9 +762,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   const float sc = sm_scale_log2_;
 
-  int twin = TREE_OFF;   // tree window of the stage being computed
   // One KV tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-  auto compute = [&](int j0, bool masked) __attribute__((always_inline)) {
+  // SO: byte offset of the stage holding the tile (a compile-time constant,
+  // so that it lands in the offset field of the LDS reads)
+  auto compute = [&](int j0, bool masked, auto so_c) __attribute__((always_inline)) {
+    constexpr int SO = decltype(so_c)::value;
+    char* const sm = smem + SO;
+    constexpr int twin = TREE_OFF + (SO ? WIN : 0);   // the tile's tree window
     // Tree masks: visibility of the 32 elements first (bit 16kb + r: element
     // r of block kb, key j0 + 32kb + 8(r/4) + 4hh + r%4), so that the test
     // overlaps the MFMAs. Causal bounds are one compare per element after.
@@ -804,9 +808,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     u32x4 kf[NF];
 #pragma unroll
     for (int t = 0; t < NF; ++t)
-      kf[t] = *reinterpret_cast<const u32x4*>(smem + (t & 1) * 32 * RB + koff[t >> 1]);
+      kf[t] = *reinterpret_cast<const u32x4*>(sm + (t & 1) * 32 * RB + koff[t >> 1]);
 #pragma unroll
     for (int t = 0; t < NF; ++t) sacc[t & 1] = mma32<BF>(kf[t], qf[t >> 1], sacc[t & 1]);
+    // V pieces of the first 16 keys, read behind the last MFMAs so that they
+    // have arrived when the softmax of this tile reaches its first PV MFMA
+    // (not with in-kernel K RoPE, whose registers are needed elsewhere)
+    constexpr bool kVEarly = !ROPE_K;
+    v4i16 v0[D / 32][2];
+    if constexpr (kVEarly) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        v0[db][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[db]));
+        v0[db][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[db] + 8 * RB));
+      }
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
 #pragma unroll
     for (int t = 0; t < NF - kAhead; ++t) {
@@ -814,6 +830,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    if constexpr (kVEarly) __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);   // the V reads
     if (masked) {
       if constexpr (MASK == kMaskTree) {
 #pragma unroll
@@ -882,9 +899,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
       }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const char* vp = smem + voff[db] + 16 * sp * RB;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * RB));
+        const char* vp = sm + voff[db] + 16 * sp * RB;
+        const bool early = kVEarly && sp == 0;
+        const v4i16 lo = early ? v0[db][0] : __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+        const v4i16 hi = early ? v0[db][1] : __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 8 * RB));
         u32x4 a;
         a[0] = __builtin_bit_cast(u32x2, lo)[0];
         a[1] = __builtin_bit_cast(u32x2, lo)[1];
@@ -895,12 +913,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // Main loop. koff / voff hold the offsets of the stage being computed and
-  // flip to the other stage (XOR STAGE, a power of two) after every tile.
-  int cur = 0;   // byte offset of the stage being computed
-  for (int it = 0; it < n_tiles; ++it) {
+  // Main loop, two tiles per trip: the stage of tile it is it % 2 (a
+  // compile-time offset), the loads for tile it + 1 go to the other one.
+  auto tile_step = [&](int it, auto so_c) __attribute__((always_inline)) {
+    constexpr int SO = decltype(so_c)::value;
+    constexpr int NSO = SO ^ STAGE;
     const int j0 = jbase + it * kBN;
-    char* next = smem + (cur ^ STAGE);
+    char* next = smem + NSO;
     wait_all_and_barrier();   // tile it is in LDS; everyone is done with tile it-1
     if (it + 1 < n_tiles) {
       issue_tile(j0 + kBN, next);
@@ -919,19 +938,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
                                                 : ((j0 + kBN <= lim_lo && j0 >= lo_max) ? 1 : 2);
     }
     cls = __builtin_amdgcn_readfirstlane(cls);
-    if (wave_active && cls != 0) compute(j0, cls == 2);
+    if (wave_active && cls != 0) compute(j0, cls == 2, so_c);
     if (it + 1 < n_tiles) {
       rope_store_k(j0 + kBN, next);
       if constexpr (MASK == kMaskTree)
-        if (tid < kBN) reinterpret_cast<int2*>(smem + (twin ^ WIN))[tid] = win_iv;
+        if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_iv;
     }
-    cur ^= STAGE;
-    twin ^= WIN;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] ^= STAGE;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) voff[db] ^= STAGE;
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_tiles) tile_step(it + 1, std::integral_constant<int, STAGE>{});
   }
+  const int cur = (n_tiles & 1) ? STAGE : 0;   // stage after the last tile
 
   // ---- epilogue: out = O / l (dtype), lse = m + log2(l) ----
   // O^T fragments go through LDS so that each row is stored as whole 16-byte

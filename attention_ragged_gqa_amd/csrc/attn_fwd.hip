@@ -182,8 +182,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   constexpr int STAGE = 2 * TILE;            // K tile, then V tile
   constexpr int RPL = 1024 / RB;             // rows one wave-wide 16-byte load covers
   constexpr int LOADS = kBN / (4 * RPL);     // per wave and tile, for K and for V each
-  // tree masks: the (enter, exit) intervals of a tile's 64 keys, one window
-  // per stage, filled alongside the K/V tile
+  // tree masks: an (enter, length) entry per key of a tile (win_entry),
+  // one window per stage, filled alongside the K/V tile
   constexpr int WIN = kBN * 8;
   constexpr int TREE_OFF = kStages * STAGE;
   constexpr int SMEM = TREE_OFF + (MASK == kMaskTree ? kStages * WIN : 0);
@@ -631,9 +631,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int my_pos = 0;
   if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
   if (n_tiles > 0) load_k_pos(jbase);
-  // tree intervals of tile 0 (raw: keys outside the tree part are decided
-  // by position in the mask test)
+  // tree intervals of tile 0 (raw; turned into window entries when stored)
   int2 win_iv = make_int2(0, 0);
+  // Window entry of chunk key kidx from its raw (enter, exit) interval:
+  // (enter, exit - enter) for tree keys, (INT_MIN, 2^32 - 1) for prefix keys
+  // (every row passes the compare), length 0 past the chunk (none does).
+  auto win_entry = [&](int kidx, int2 iv) __attribute__((always_inline)) -> int2 {
+    if (kidx >= kv_len) return make_int2(INT_MAX, 0);
+    if (kidx < tree_start) return make_int2(INT_MIN, -1);
+    const unsigned len = iv.y > iv.x ? static_cast<unsigned>(iv.y) - static_cast<unsigned>(iv.x) : 0u;
+    return make_int2(iv.x, static_cast<int>(len));
+  };
   if constexpr (MASK == kMaskTree)
     win_iv = load_i32x2(tree_rsrc, tree_base + jbase + (tid & (kBN - 1)) - tree_start);
 
@@ -688,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   if constexpr (MASK == kMaskTree) {
     pin(win_iv.x);
     pin(win_iv.y);
-    if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF)[tid] = win_iv;
+    if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF)[tid] = win_entry(jbase + tid, win_iv);
   }
   int enter_c = INT_MIN;   // sentinel: sees the prefix only
   if constexpr (MASK == kMaskTree) {
@@ -769,36 +777,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     constexpr int SO = decltype(so_c)::value;
     char* const sm = smem + SO;
     constexpr int twin = TREE_OFF + (SO ? WIN : 0);   // the tile's tree window
-    // Tree masks: visibility of the 32 elements first (bit 16kb + r: element
-    // r of block kb, key j0 + 32kb + 8(r/4) + 4hh + r%4), so that the test
-    // overlaps the MFMAs. Causal bounds are one compare per element after.
-    unsigned vbits = ~0u;
-    if (MASK == kMaskTree && masked) {   // uniform: only partial tiles test each element
-      asm volatile("");   // keeps this a branch (the compiler would otherwise select)
-      vbits = 0u;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int kq = j0 + 32 * kb + 8 * q4 + 4 * hh;   // 4 consecutive keys
-          if constexpr (MASK == kMaskTree) {
-            const u32x4* wp = reinterpret_cast<const u32x4*>(smem + twin + 8 * (kq - j0));
-            const u32x4 a = wp[0], c = wp[1];
-            const int ex[4] = {static_cast<int>(a[0]), static_cast<int>(a[2]), static_cast<int>(c[0]),
-                               static_cast<int>(c[2])};
-            const int xx[4] = {static_cast<int>(a[1]), static_cast<int>(a[3]), static_cast<int>(c[1]),
-                               static_cast<int>(c[3])};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int kidx = kq + u;
-              const bool vis = (kidx < kv_len) &
-                               ((kidx < tree_start) | ((enter_c >= ex[u]) & (enter_c < xx[u])));
-              vbits |= static_cast<unsigned>(vis) << (16 * kb + 4 * q4 + u);
-            }
-          }
-        }
-      }
-    }
     // The two 32-key blocks alternate, so consecutive MFMAs are independent,
     // and every K fragment is read kAhead MFMAs before its use: the LDS
     // latency hides behind the MFMAs instead of stalling each one.
@@ -833,11 +811,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     if constexpr (kVEarly) __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);   // the V reads
     if (masked) {
       if constexpr (MASK == kMaskTree) {
+        // element r of block kb is key j0 + 32kb + 8(r/4) + 4hh + r%4; its
+        // window entry (enter, length) makes the ancestor test one unsigned
+        // compare: visible iff enter_c - enter < length
+        const unsigned ec = static_cast<unsigned>(enter_c);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((vbits >> (16 * kb + r)) & 1u)) sacc[kb][r] = -INFINITY;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4* wp = reinterpret_cast<const u32x4*>(smem + twin + 8 * (32 * kb + 8 * q4 + 4 * hh));
+            const u32x4 a = wp[0], c = wp[1];
+            const unsigned ex[4] = {a[0], a[2], c[0], c[2]};
+            const unsigned ln[4] = {a[1], a[3], c[1], c[3]};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (!(ec - ex[u] < ln[u])) sacc[kb][4 * q4 + u] = -INFINITY;
+          }
+        }
       } else {
         // key j0 + 4hh + c(kb, r) is visible iff lo - j0 - 4hh <= c < lim - j0 - 4hh
         const int rel = lim - j0 - 4 * hh;
@@ -942,7 +932,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     if (it + 1 < n_tiles) {
       rope_store_k(j0 + kBN, next);
       if constexpr (MASK == kMaskTree)
-        if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_iv;
+        if (tid < kBN)
+          reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_entry(j0 + kBN + tid, win_iv);
     }
   };
   for (int it = 0; it < n_tiles; it += 2) {

@@ -114,14 +114,15 @@ __device__ __forceinline__ float pair_sum(float x) {
 // ---- rotary embedding ------------------------------------------------------
 // Rotate-half RoPE of the "_kernel_common.py" page (_rope): for dims k and
 // k + D/2 the angle is float32(pos * scale) * inv_freq[k] with
-// inv_freq[k] = theta^(-2k/D). cos and sin are evaluated in float64 and
-// rounded once to float32, so they are the correctly rounded float32 values
-// except within ~1e-13 (relative) of a rounding boundary:
+// inv_freq[k] = theta^(-2k/D).
 //   angle = pos_f * inv_freq (float64), n = nearest integer to angle/(pi/2),
 //   r = angle - n*pi/2 with pi/2 split in two parts (|r| <= pi/4 + tiny),
-//   sin r through r^15 and cos r through r^14 from their Taylor series
-//   (relative truncation below 2e-15 on |r| <= pi/4), rounded to float32,
-//   then the quadrant n mod 4 swaps and negates them.
+//   all in float64, so r is accurate to ~1e-16 relative even for large
+//   positions; then r is rounded to float32 and sin r, cos r come from their
+//   Taylor series in float32 (sin through r^9, cos through r^10: truncation
+//   below 2e-9 on |r| <= pi/4), and the quadrant n mod 4 swaps and negates
+//   them. Against the correctly rounded float32 cos and sin the error is
+//   below 1e-7 absolute (at most one float32 ulp away from zero crossings).
 // n is taken as an int32, which holds it while |angle| < 3e9 (any int32
 // position with scale <= 1).
 // The rotated value is evaluated in float32 as cos*x + sin*partner (two
@@ -134,26 +135,23 @@ __device__ __forceinline__ void rope_cos_sin(int pos, float scale, double inv_fr
   const double kPio2Hi = 1.5707963267948966;       // float64(pi/2)
   const double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
   const double n = rint(ang * 0.6366197723675814);  // 2/pi
-  double r = fma(-n, kPio2Hi, ang);
-  r = fma(-n, kPio2Lo, r);
-  const double r2 = r * r;
-  // sin r = r - r^3/3! + r^5/5! - ... ; cos r = 1 - r^2/2! + r^4/4! - ...
-  double sp = -7.647163731819816e-13;               // -1/15!
-  sp = fma(sp, r2, 1.6059043836821613e-10);         //  1/13!
-  sp = fma(sp, r2, -2.505210838544172e-08);         // -1/11!
-  sp = fma(sp, r2, 2.7557319223985893e-06);         //  1/9!
-  sp = fma(sp, r2, -1.984126984126984e-04);         // -1/7!
-  sp = fma(sp, r2, 8.333333333333333e-03);          //  1/5!
-  sp = fma(sp, r2, -1.6666666666666666e-01);        // -1/3!
-  const float sr = static_cast<float>(fma(sp * r2, r, r));
-  double cp = -1.1470745597729725e-11;              // -1/14!
-  cp = fma(cp, r2, 2.08767569878681e-09);           //  1/12!
-  cp = fma(cp, r2, -2.755731922398589e-07);         // -1/10!
-  cp = fma(cp, r2, 2.48015873015873e-05);           //  1/8!
-  cp = fma(cp, r2, -1.388888888888889e-03);         // -1/6!
-  cp = fma(cp, r2, 4.1666666666666664e-02);         //  1/4!
-  cp = fma(cp, r2, -0.5);                           // -1/2!
-  const float cr = static_cast<float>(fma(cp, r2, 1.0));
+  double rd = fma(-n, kPio2Hi, ang);
+  rd = fma(-n, kPio2Lo, rd);
+  const float r = static_cast<float>(rd);
+  const float r2 = r * r;
+  // sin r = r - r^3/3! + r^5/5! - r^7/7! + r^9/9!
+  float sp = 2.7557319e-06f;                        //  1/9!
+  sp = fmaf(sp, r2, -1.9841270e-04f);               // -1/7!
+  sp = fmaf(sp, r2, 8.3333333e-03f);                //  1/5!
+  sp = fmaf(sp, r2, -1.6666667e-01f);               // -1/3!
+  const float sr = fmaf(sp * r2, r, r);
+  // cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
+  float cp = -2.7557319e-07f;                       // -1/10!
+  cp = fmaf(cp, r2, 2.4801587e-05f);                //  1/8!
+  cp = fmaf(cp, r2, -1.3888889e-03f);               // -1/6!
+  cp = fmaf(cp, r2, 4.1666668e-02f);                //  1/4!
+  cp = fmaf(cp, r2, -0.5f);                         // -1/2!
+  const float cr = fmaf(cp, r2, 1.0f);
   const int q = static_cast<int>(n) & 3;
   const float sv = (q & 1) ? cr : sr;
   const float cv = (q & 1) ? sr : cr;

@@ -110,6 +110,12 @@ PAGED_CASES = [
          rotary_mode=1, k_rope_pos_offset=[5, 100, 2000]),
     dict(seed=21, qo=[300, 44], stored=[900, 44], h_q=32, h_kv=8, d=128, dtype="bf16", causal=1,
          store_rope="linear", rope_theta=1e4),
+    # sliding windows whose (offset - sink) is not a multiple of 16: the tile
+    # grid is shifted by that remainder; sinks longer than one 16-row block
+    dict(seed=22, qo=[33, 70], stored=[500, 260], h_q=8, h_kv=2, d=64, dtype="f16", causal=1,
+         sliding=([321, 77], [21, 3])),
+    dict(seed=23, qo=[5, 129, 64], stored=[777, 1000, 700], h_q=16, h_kv=4, d=128, dtype="bf16", causal=1,
+         sliding=([511, 690, 650], [1, 7, 16])),
 ]
 
 

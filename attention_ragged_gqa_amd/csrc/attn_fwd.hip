@@ -32,12 +32,18 @@
 //    consecutive keys of one dim per lane) reads 4 rows x 32 bytes per
 //    16-lane group without conflicts (both measured). With in-kernel K RoPE
 //    the K tile is rotated in registers and written instead.
+//  * Paged KV: each wave loads a 16-row block per tile, which with page size
+//    16 is one page; sliding windows shift the tile grid so that this holds
+//    past the sink. Other blocks (sink rows, ragged ends, bad pages) are
+//    loaded row by row.
 //  * Masks are classified per (wave, tile): skipped, full (no test) or
-//    partial (per-element test); causal work stops at the last visible tile.
-//    Tree intervals of the sequence are staged in LDS once.
+//    partial (per-element test); causal work stops at the last visible tile
+//    (and, with left padding, starts at the first). Tree masks use a
+//    per-stage LDS window of (enter, length) per key of the tile.
 //  * The softmax runs in the log2 domain (v_exp_f32 is exp2): scores are
-//    scaled by sm_scale*log2(e), lse = m + log2(l) as on the pages; the O
-//    rescale is skipped when no row of the wave has a new max.
+//    scaled by sm_scale*log2(e), lse = m + log2(l) as on the pages; the
+//    running max only moves (and O is rescaled) when a tile raises it by
+//    more than kRescaleSlack.
 
 #include <climits>
 #include <cmath>

@@ -250,7 +250,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=str(DEFAULT_CONFIG),
-                    help="0..4, or an extra workload name (paged_decode)")
+                    help="0..4, or an extra workload name (paged_decode, ragged_left_padded)")
     ap.add_argument("--split", type=int, default=None,
                     help="split-KV count for paged workloads (0: auto, -1: unsplit entry point); "
                          "default: auto for paged_decode, unsplit otherwise")

@@ -562,8 +562,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
   };
   // The partner lanes (chunks c and c ^ CH/2 of one row) need the same 8
-  // frequencies: each evaluates 4 of them and they swap the results.
-  auto rope_store_k = [&](int j0, char* stage) __attribute__((always_inline)) {
+  // frequencies: each evaluates 4 of them and they swap the results, or,
+  // with from_tab, both read them from the (cos, sin) table of the tile's
+  // rows in the other stage (built in the prologue, row r = tile row r).
+  auto rope_store_k = [&](int j0, char* stage, bool from_tab) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
@@ -571,24 +573,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
         const int kidx = j0 + r;
         const int lc = pc ^ KSWZ(r);               // logical chunk held
         const bool first = lc < CH / 2;
-        int kp = kpos[i];
-        pin(kp);
-        const int pos = kidx < kv_len ? kp : 0;
-        // frequencies 8*(lc mod CH/2) + e; this lane evaluates e in [emine, emine + 4)
-        const int kbase = 8 * (lc & (CH / 2 - 1));
-        const int emine = first ? 0 : 4;
-        float cmine[4], smine[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) rope_cos_sin(pos, rope_scale_, inv_freq_s[kbase + emine + u], cmine[u], smine[u]);
         float cs[8], sn[8];
+        if (from_tab) {
+          // frequencies 8*(lc mod CH/2) + [0, 8): one 8-entry chunk of row r
+          const float4* tc = reinterpret_cast<const float4*>(smem + STAGE) + r * (D / 4) +
+                             4 * (((lc & (CH / 2 - 1)) + r) & (D / 16 - 1));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float co = __shfl_xor(cmine[u], CH / 2, 64);
-          const float so = __shfl_xor(smine[u], CH / 2, 64);
-          cs[u] = first ? cmine[u] : co;
-          sn[u] = first ? smine[u] : so;
-          cs[u + 4] = first ? co : cmine[u];
-          sn[u + 4] = first ? so : smine[u];
+          for (int v = 0; v < 4; ++v) {
+            const float4 x = tc[v];
+            cs[2 * v] = x.x;
+            sn[2 * v] = x.y;
+            cs[2 * v + 1] = x.z;
+            sn[2 * v + 1] = x.w;
+          }
+        } else {
+          int kp = kpos[i];
+          pin(kp);
+          const int pos = kidx < kv_len ? kp : 0;
+          // frequencies 8*(lc mod CH/2) + e; this lane evaluates e in [emine, emine + 4)
+          const int kbase = 8 * (lc & (CH / 2 - 1));
+          const int emine = first ? 0 : 4;
+          float cmine[4], smine[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            rope_cos_sin(pos, rope_scale_, inv_freq_s[kbase + emine + u], cmine[u], smine[u]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float co = __shfl_xor(cmine[u], CH / 2, 64);
+            const float so = __shfl_xor(smine[u], CH / 2, 64);
+            cs[u] = first ? cmine[u] : co;
+            sn[u] = first ? smine[u] : so;
+            cs[u + 4] = first ? co : cmine[u];
+            sn[u + 4] = first ? so : smine[u];
+          }
         }
         u32x4 other;
 #pragma unroll
@@ -619,24 +636,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const int t_first = row0 / g;
   const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
   const int n_tok = max(t_end - t_first, 0);
-  // Q RoPE table (cos, sin) per (token of this tile, frequency) in stage 1,
-  // shared by the g heads of a token; with g = 1 each lane computes its own.
-  const bool q_table = rope_q_ && n_tok * (D / 2) * 8 <= STAGE;
+  // RoPE table (cos, sin) per (row, frequency) in stage 1. Q table: one row
+  // per token of this tile, shared by the g heads of a token (with g = 1
+  // each lane computes its own). With in-kernel K RoPE on contiguous KV, K
+  // row j of the chunk rotates at position entry kv_base + j; when the
+  // tile's query tokens index entries of the first K tile's range, one
+  // table over that tile's 64 rows serves K and Q alike (KQ table): query
+  // token t reads row kq0 + t - t_first.
+  const int kq0 = q0 + t_first - (kv_base + jbase);
+  const bool kq_table = ROPE_K && LAYOUT == kContiguous && rope_q_ && n_tiles > 0 && kq0 >= 0 &&
+                        kq0 + n_tok <= kBN;
+  const bool q_table = rope_q_ && !kq_table && n_tok * (D / 2) * 8 <= STAGE;
+  const int tab_pos0 = kq_table ? kv_base + jbase : q0 + t_first;   // position entry of table row 0
   // Order of the prologue loads. Positions first (the RoPE tables need only
   // them). Paged: the tile-0 addresses need the page numbers, so the pages
-  // go next and tile 0 is issued when they arrive, then Q. Contiguous: Q,
-  // then tile 0. (Loads complete in issue order, so whatever a wait needs
-  // should have gone out early.)
+  // go next and tile 0 is issued when they arrive, then Q. Contiguous: with
+  // in-kernel K RoPE the K rows (rotated, then stored, before the first
+  // tile), then Q, then V; otherwise Q, then tile 0. (Loads complete in
+  // issue order, so whatever a wait needs should have gone out early.)
   constexpr int TPOS = STAGE / 8 / kThreads;   // table entries per thread at most
   static_assert(TPOS * kThreads * 8 == STAGE, "table entries per thread");
+  static_assert(kBN * (D / 2) == TPOS * kThreads, "KQ table rows");
   int tpos[TPOS];                                // token positions of those entries
-  if (q_table) {
+  if (q_table || kq_table) {
 #pragma unroll
-    for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, q0 + t_first + (tid + u * kThreads) / (D / 2));
+    for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, tab_pos0 + (tid + u * kThreads) / (D / 2));
   }
   int my_pos = 0;
   if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
-  if (n_tiles > 0) load_k_pos(jbase);
+  if (n_tiles > 0 && !kq_table) load_k_pos(jbase);
   // tree intervals of tile 0 (raw; turned into window entries when stored)
   int2 win_iv = make_int2(0, 0);
   // Window entry of chunk key kidx from its raw (enter, exit) interval:
@@ -654,7 +682,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   auto issue_first_tile = [&]() __attribute__((always_inline)) {
     if (n_tiles > 0) {
       issue_tile(jbase, smem);                             // V (and K) straight into stage 0
-      load_k_regs(jbase);
+      if (LAYOUT == kPaged || !ROPE_K) load_k_regs(jbase);
       if (n_tiles > 1) page_next = fetch_page(jbase + kBN);   // page of the second tile
     }
   };
@@ -663,6 +691,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     // one wait for the page number here, before the tile-0 loads go out
     pin(page_next);
     issue_first_tile();
+  } else if constexpr (ROPE_K) {
+    if (n_tiles > 0) load_k_regs(jbase);
   }
 
   // ---- Q fragments: lane holds row R, dims 16*s + 8*hh + [0, 8) ----
@@ -682,14 +712,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   }
   __syncthreads();   // inv_freq is visible (the loads above are still in flight)
 
-  if (q_table) {
+  if (q_table || kq_table) {
     float2* tab = reinterpret_cast<float2*>(smem + STAGE);
+    const int n_ent = (kq_table ? kBN : n_tok) * (D / 2);
 #pragma unroll
     for (int u = 0; u < TPOS; ++u) pin(tpos[u]);
 #pragma unroll
     for (int u = 0; u < TPOS; ++u) {
       const int e = tid + u * kThreads;
-      if (e < n_tok * (D / 2)) {
+      if (e < n_ent) {
         float cs, sn;
         rope_cos_sin(tpos[u], rope_scale_, inv_freq_s[e % (D / 2)], cs, sn);
         // 8-entry chunks of a token's row rotated by the token index, so
@@ -709,19 +740,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     pin(enter_raw);
     if (row_ok && c_node >= 0 && c_node < tree_len) enter_c = enter_raw;
   }
-  if (n_tiles > 0) rope_store_k(jbase, smem);
+  if (kq_table) __syncthreads();   // the table is visible to every wave
+  if (n_tiles > 0) rope_store_k(jbase, smem, kq_table);
   if (rope_q_) {
     if (q_table) __syncthreads();
     pin(my_pos);
     if (row_ok) {
-      const int tr = t - t_first;
+      const int tr = t - t_first + (kq_table ? kq0 : 0);
       const float4* trow = reinterpret_cast<const float4*>(smem + STAGE) + tr * (D / 4);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const u32x4 a = qf[s], c2 = qf[s + D / 32];
         // frequencies 16s + 8hh + [0, 8): one 8-entry chunk of the table row
         float cs[8], sn[8];
-        if (q_table) {
+        if (q_table || kq_table) {
           const float4* tc = trow + 4 * (((2 * s + hh) + tr) & (D / 16 - 1));
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -936,7 +968,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     cls = __builtin_amdgcn_readfirstlane(cls);
     if (wave_active && cls != 0) compute(j0, cls == 2, so_c);
     if (it + 1 < n_tiles) {
-      rope_store_k(j0 + kBN, next);
+      rope_store_k(j0 + kBN, next, false);
       if constexpr (MASK == kMaskTree)
         if (tid < kBN)
           reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_entry(j0 + kBN + tid, win_iv);

@@ -30,6 +30,7 @@ __all__ = [
     "ra_paged_attn_split_workspace",
     "ra_merge_states",
     "ra_paged_kv_append",
+    "ra_set_workgroup_waves",
     "ra_last_error",
 ]
 
@@ -38,7 +39,7 @@ LIB_NAME = "libragattn.so"
 
 EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
                     "ra_paged_attn_split_workspace", "ra_merge_states", "ra_paged_kv_append",
-                    "ra_last_error")
+                    "ra_set_workgroup_waves", "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
 RA_F16, RA_BF16 = 0, 1
@@ -86,6 +87,8 @@ def library() -> ctypes.CDLL:
     lib.ra_merge_states.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.ra_paged_kv_append.restype = i32
     lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
+    lib.ra_set_workgroup_waves.restype = i32
+    lib.ra_set_workgroup_waves.argtypes = [i32]
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_last_error.argtypes = []
     _lib = lib
@@ -94,6 +97,16 @@ def library() -> ctypes.CDLL:
 
 def ra_last_error() -> str:
     return library().ra_last_error().decode()
+
+
+def ra_set_workgroup_waves(waves: int) -> None:
+    """Fix the attention kernels' workgroup shape for later launches in this
+    process: 4 or 8 waves (128 or 256 packed query rows per work item), or 0
+    to let each launch choose (the default). A tuning override; results are
+    the same either way."""
+    st = library().ra_set_workgroup_waves(int(waves))
+    if st != RA_OK:
+        raise RagAttnError(st, ra_last_error())
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -45,6 +45,7 @@
 //    running max only moves (and O is rescaled) when a tile raises it by
 //    more than kRescaleSlack.
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -126,7 +127,7 @@ __device__ __forceinline__ int t_first_of(int row0, int g) { return row0 / g; }
 // share an XCD's L2.
 // With split-KV (splits > 1) each q-tile is `splits` items, one per KV range.
 // Also returns the sequence's query offset q0 and length qo_len.
-__device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int splits,
+__device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int splits, int bm,
                             int& b, int& kvh, int& tile, int& split, int& q0, int& qo_len) {
   const int lane = threadIdx.x & 63;
   // q-tiles of sequence i, and its query range
@@ -136,7 +137,7 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
     if (i >= batch) return 0;
     lo = q_indptr[i];
     len = max(q_indptr[i + 1] - lo, 0);
-    return (len * group + kBM - 1) / kBM * splits;
+    return (len * group + bm - 1) / bm * splits;
   };
   int lo0, len0;
   const int cnt0 = count(lane, lo0, len0);   // first 64 sequences, kept for the search
@@ -180,20 +181,27 @@ __device__ bool locate_item(const int32_t* q_indptr, int batch, int group, int h
   return false;
 }
 
-template <bool BF, int D, int LAYOUT, int MASK, bool ROPE_K>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
+// NW waves per workgroup (4 or 8; two or one workgroups per CU): the work
+// item is BM = 32 NW packed query rows, and each wave loads kBN / NW rows of
+// every K/V tile, so eight waves issue half the K/V loads per query row.
+template <int NW, bool BF, int D, int LAYOUT, int MASK, bool ROPE_K>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p) {
+  constexpr int NT = 64 * NW;                // threads
+  constexpr int BM = 32 * NW;                // packed query rows per work item
+  constexpr int RW = kBN / NW;               // rows of a K/V tile each wave loads
   constexpr int RB = D * 2;                  // bytes per head row
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = kBN * RB;             // bytes of one K or V tile
   constexpr int STAGE = 2 * TILE;            // K tile, then V tile
   constexpr int RPL = 1024 / RB;             // rows one wave-wide 16-byte load covers
-  constexpr int LOADS = kBN / (4 * RPL);     // per wave and tile, for K and for V each
+  constexpr int LOADS = kBN / (NW * RPL);    // per wave and tile, for K and for V each
   // tree masks: an (enter, length) entry per key of a tile (win_entry),
   // one window per stage, filled alongside the K/V tile
   constexpr int WIN = kBN * 8;
   constexpr int TREE_OFF = kStages * STAGE;
   constexpr int SMEM = TREE_OFF + (MASK == kMaskTree ? kStages * WIN : 0);
-  static_assert(LOADS >= 1 && 4 * RPL * LOADS == kBN, "tile shape");
+  static_assert(LOADS >= 1 && NW * RPL * LOADS == kBN, "tile shape");
+  static_assert(16 % RW == 0, "a wave's block of a tile lies within one page");
   static_assert((STAGE & (STAGE - 1)) == 0, "stage size is a power of two");
   // LDS chunk swizzles (see the header comment): K chunk c of row r sits at
   // c ^ KSWZ(r), V chunk c at c ^ VSWZ(r); RSH = log2(rows per 256 bytes).
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 
   const int splits = max(p.num_splits, 1);
   int b = 0, kvh = 0, tile = 0, split_m = 0, q0_m = 0, qo_len_m = 0;
-  if (!locate_item(q_indptr_, batch_, group_, h_kv_, splits, b, kvh, tile, split_m, q0_m, qo_len_m))
+  if (!locate_item(q_indptr_, batch_, group_, h_kv_, splits, BM, b, kvh, tile, split_m, q0_m, qo_len_m))
     return;   // uniform over the workgroup
   b = __builtin_amdgcn_readfirstlane(b);
   kvh = __builtin_amdgcn_readfirstlane(kvh);
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   const int g = group_;
   const int q0 = __builtin_amdgcn_readfirstlane(q0_m);
   const int qo_len = __builtin_amdgcn_readfirstlane(qo_len_m);
-  const int row0 = tile * kBM;
+  const int row0 = tile * BM;
 
   // ---- KV chunk of this sequence ----
   // The per-sequence scalars come in one vector load (lane i fetches value i)
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int lo_m = 0;
   int kv_hi = kv_len;
   int kv_lo = 0;   // first key any row of the tile can see
-  const int t_last = min((row0 + kBM - 1) / g, qo_len - 1);
+  const int t_last = min((row0 + BM - 1) / g, qo_len - 1);
   if (causal) kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
   if (pad_mode == 1) {          // right padding: rows and keys below valid_len
     const int vl = min(max(valid_m, 0), kv_len);
@@ -400,19 +408,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   int enter_raw = 0;
   if constexpr (MASK == kMaskTree) enter_raw = load_i32x2(tree_rsrc, tree_base + c_node).x;
 
-  // ---- K/V tile loads: wave w fills tile rows [16w, 16w + 16); lane covers
-  // rows 16w + RPL*i + lane/CH (i < LOADS) at physical chunk lane % CH ----
+  // ---- K/V tile loads: wave w fills tile rows [RW w, RW w + RW); lane covers
+  // rows RW w + RPL*i + lane/CH (i < LOADS) at physical chunk lane % CH ----
   const int pc = lane % CH;
   const int lrow = lane / CH;
-  auto tile_row = [&](int i) __attribute__((always_inline)) { return 16 * w + RPL * i + lrow; };
-  // Page of the wave's 16-row block [B, B + 16) of a tile, B = j0 + 16w.
-  // Past the sink such a block is one whole page (storage offsets
-  // B + delta, a multiple of 16 on the shifted grid). The page number is
+  auto tile_row = [&](int i) __attribute__((always_inline)) { return RW * w + RPL * i + lrow; };
+  // Page of the wave's RW-row block [B, B + RW) of a tile, B = j0 + RW w.
+  // Past the sink such a block lies within one page (storage offsets from
+  // B + delta; j0 + delta is a multiple of 16 on the shifted grid and RW
+  // divides 16). The page number is
   // loaded a tile ahead and only read (v_readfirstlane) when the block is
   // issued; out-of-range indices read 0 and are rejected there.
   const __amdgpu_buffer_rsrc_t page_rsrc = make_rsrc(page_values_, 4L * nnz_pages_);
   auto fetch_page = [&](int j0) __attribute__((always_inline)) -> int {
-    if constexpr (LAYOUT == kPaged) return load_i32(page_rsrc, page_base + ((j0 + 16 * w + delta) >> 4));
+    if constexpr (LAYOUT == kPaged) return load_i32(page_rsrc, page_base + ((j0 + RW * w + delta) >> 4));
     else return 0;
   };
   int page_next = 0;   // page of this wave's block of the next tile to issue
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     kv_head_v = kv_head_k + static_cast<size_t>(h_kv_) * 16 * RB;
   }
   const size_t v_minus_k = static_cast<size_t>(kv_head_v - kv_head_k);
-  // Blocks that take the whole-block path: B in [fast_lo, fast_hi - 16] and,
+  // Blocks that take the whole-block path: B in [fast_lo, fast_hi - RW] and,
   // when paged, a page number below num_pages. Everything else (sink rows,
   // keys j < 0, the chunk's ragged end, rows of pages outside the sequence's
   // range or past the cache) goes row by row.
@@ -440,13 +449,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     fast_hi = min(kv_len, (page_end - page_base) * 16 - delta);
   }
   auto block_fast = [&](int B, int pg) __attribute__((always_inline)) -> bool {
-    const bool rows = B >= fast_lo && B + 16 <= fast_hi;
+    const bool rows = B >= fast_lo && B + RW <= fast_hi;
     if constexpr (LAYOUT == kPaged) return rows && static_cast<unsigned>(pg) < static_cast<unsigned>(num_pages_);
     else return rows;
   };
   auto block_base = [&](int B, int pg) __attribute__((always_inline)) -> const char* {
     if constexpr (LAYOUT == kContiguous) return kv_head_k + static_cast<size_t>(B) * kv_stride;
-    else return kv_head_k + static_cast<size_t>(static_cast<uint32_t>(pg)) * page_stride;
+    else
+      return kv_head_k + static_cast<size_t>(static_cast<uint32_t>(pg)) * page_stride + ((B + delta) & 15) * RB;
   };
   // Per-row K source of chunk position kidx (V: + v_minus_k), or null for a
   // row outside the chunk or with an invalid page. page: the page number
@@ -494,13 +504,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   };
 
   auto issue_tile = [&](int j0, char* stage) __attribute__((always_inline)) {
-    const int B = j0 + 16 * w;
+    const int B = j0 + RW * w;
     const int pg = __builtin_amdgcn_readfirstlane(page_next);
     if (block_fast(B, pg)) {
       const char* base = block_base(B, pg);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        char* dst_k = stage + (16 * w + RPL * i) * RB;          // wave-uniform
+        char* dst_k = stage + (RW * w + RPL * i) * RB;          // wave-uniform
         if constexpr (!ROPE_K) dma16s(base, lane_off(i, false), dst_k);
         dma16s(base + v_minus_k, lane_off(i, true), dst_k + TILE);
       }
@@ -510,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int r = tile_row(i);
-        char* dst_k = stage + (16 * w + RPL * i) * RB;
+        char* dst_k = stage + (RW * w + RPL * i) * RB;
         const char* src = row_src(j0 + r, rp[i]);
         if (src) {
           if constexpr (!ROPE_K) dma16(src + 16 * (pc ^ KSWZ(r)), dst_k);
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   };
   auto load_k_regs = [&](int j0) __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
-      const int B = j0 + 16 * w;
+      const int B = j0 + RW * w;
       const int pg = __builtin_amdgcn_readfirstlane(page_next);
       if (block_fast(B, pg)) {
         const char* base = block_base(B, pg);
@@ -634,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // ---- prologue: every load that depends only on the sequence goes out
   // together; tile 0 is in flight while RoPE tables are computed ----
   const int t_first = row0 / g;
-  const int t_end = min((row0 + kBM - 1) / g + 1, qo_len);
+  const int t_end = min((row0 + BM - 1) / g + 1, qo_len);
   const int n_tok = max(t_end - t_first, 0);
   // RoPE table (cos, sin) per (row, frequency) in stage 1. Q table: one row
   // per token of this tile, shared by the g heads of a token (with g = 1
@@ -654,13 +664,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
   // in-kernel K RoPE the K rows (rotated, then stored, before the first
   // tile), then Q, then V; otherwise Q, then tile 0. (Loads complete in
   // issue order, so whatever a wait needs should have gone out early.)
-  constexpr int TPOS = STAGE / 8 / kThreads;   // table entries per thread at most
-  static_assert(TPOS * kThreads * 8 == STAGE, "table entries per thread");
-  static_assert(kBN * (D / 2) == TPOS * kThreads, "KQ table rows");
+  constexpr int TPOS = STAGE / 8 / NT;         // table entries per thread at most
+  static_assert(TPOS * NT * 8 == STAGE, "table entries per thread");
+  static_assert(kBN * (D / 2) == TPOS * NT, "KQ table rows");
   int tpos[TPOS];                                // token positions of those entries
   if (q_table || kq_table) {
 #pragma unroll
-    for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, tab_pos0 + (tid + u * kThreads) / (D / 2));
+    for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, tab_pos0 + (tid + u * NT) / (D / 2));
   }
   int my_pos = 0;
   if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
@@ -719,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     for (int u = 0; u < TPOS; ++u) pin(tpos[u]);
 #pragma unroll
     for (int u = 0; u < TPOS; ++u) {
-      const int e = tid + u * kThreads;
+      const int e = tid + u * NT;
       if (e < n_ent) {
         float cs, sn;
         rope_cos_sin(tpos[u], rope_scale_, inv_freq_s[e % (D / 2)], cs, sn);
@@ -1009,7 +1019,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
     }
     return;
   }
-  char* obuf = smem + cur + (32 * w) * RB;   // this wave's 32 rows, same swizzle as K
+  // This wave's 32 rows, same swizzle as K. Four waves fit in the stage at
+  // `cur`; eight need both stages, once every wave is done with the last tile.
+  char* obuf = smem + cur + (32 * w) * RB;
+  if constexpr (NW == 8) {
+    static_assert(NW * 32 * RB == kStages * STAGE, "eight waves' rows fill both stages");
+    __syncthreads();
+    obuf = smem + (32 * w) * RB;
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1046,44 +1063,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnParams p) {
 #undef KSWZ
 #undef VSWZ
 
-template <bool BF, int D, int LAYOUT, int MASK>
+template <int NW, bool BF, int D, int LAYOUT, int MASK>
 void launch_r(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (p.rope_k)
-    hipLaunchKernelGGL((attn_fwd_kernel<BF, D, LAYOUT, MASK, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<NW, BF, D, LAYOUT, MASK, true>), grid, dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<BF, D, LAYOUT, MASK, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<NW, BF, D, LAYOUT, MASK, false>), grid, dim3(64 * NW), 0, stream, p);
 }
 
-template <bool BF, int D>
-hipError_t launch_d(const AttnParams& p, KvLayout layout, MaskKind mask, dim3 grid,
-                    hipStream_t stream) {
+template <int NW, bool BF, int D>
+void launch_d(const AttnParams& p, KvLayout layout, MaskKind mask, dim3 grid, hipStream_t stream) {
   if (layout == kContiguous) {
-    if (mask == kMaskTree) launch_r<BF, D, kContiguous, kMaskTree>(p, grid, stream);
-    else launch_r<BF, D, kContiguous, kMaskCausal>(p, grid, stream);
+    if (mask == kMaskTree) launch_r<NW, BF, D, kContiguous, kMaskTree>(p, grid, stream);
+    else launch_r<NW, BF, D, kContiguous, kMaskCausal>(p, grid, stream);
   } else {
-    if (mask == kMaskTree) launch_r<BF, D, kPaged, kMaskTree>(p, grid, stream);
-    else launch_r<BF, D, kPaged, kMaskCausal>(p, grid, stream);
+    if (mask == kMaskTree) launch_r<NW, BF, D, kPaged, kMaskTree>(p, grid, stream);
+    else launch_r<NW, BF, D, kPaged, kMaskCausal>(p, grid, stream);
+  }
+}
+
+template <int NW>
+hipError_t launch_nw(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout, MaskKind mask,
+                     hipStream_t stream) {
+  // Upper bound on the number of work items, plus slack so that the
+  // XCD-contiguous mapping (8 * ceil(items / 8) blocks) always fits.
+  constexpr long bm = 32 * NW;
+  const long tiles = (static_cast<long>(p.total_q) * p.group + bm - 1) / bm + p.batch;
+  long blocks = tiles * p.h_kv * (p.num_splits > 1 ? p.num_splits : 1) + 7;
+  blocks = (blocks + 7) / 8 * 8;
+  if (blocks > INT_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (is_bf16) {
+    if (head_dim == 128) launch_d<NW, true, 128>(p, layout, mask, grid, stream);
+    else launch_d<NW, true, 64>(p, layout, mask, grid, stream);
+  } else {
+    if (head_dim == 128) launch_d<NW, false, 128>(p, layout, mask, grid, stream);
+    else launch_d<NW, false, 64>(p, layout, mask, grid, stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Eight-wave workgroups load each K/V tile once for 256 query rows (half the
+// loads per row) but are one per CU, so they pay off only when the 256-row
+// items cover the 256 CUs at least twice; split-KV ranges are short and use
+// four waves. (The item count here ignores ragged tails: a lower bound.)
+namespace {
+std::atomic<int> g_waves_override{0};
+}  // namespace
+
+void set_waves_override(int waves) { g_waves_override.store(waves, std::memory_order_relaxed); }
+
+int waves_per_item(const AttnParams& p) {
+  constexpr long kCUs = 256;   // MI355X
+  if (p.num_splits > 1) return 4;
+  const int forced = g_waves_override.load(std::memory_order_relaxed);
+  if (forced != 0) return forced;
+  const long items8 = (static_cast<long>(p.total_q) * p.group + 255) / 256 * p.h_kv;
+  return items8 >= 2 * kCUs ? 8 : 4;
+}
+
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
                        MaskKind mask, hipStream_t stream) {
-  // Upper bound on the number of work items, plus slack so that the
-  // XCD-contiguous mapping (8 * ceil(items / 8) blocks) always fits.
-  const long tiles = (static_cast<long>(p.total_q) * p.group + kBM - 1) / kBM + p.batch;
-  long blocks = tiles * p.h_kv * (p.num_splits > 1 ? p.num_splits : 1) + 7;
-  blocks = (blocks + 7) / 8 * 8;
-  if (blocks > INT_MAX) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  if (is_bf16) {
-    return head_dim == 128 ? launch_d<true, 128>(p, layout, mask, grid, stream)
-                           : launch_d<true, 64>(p, layout, mask, grid, stream);
-  }
-  return head_dim == 128 ? launch_d<false, 128>(p, layout, mask, grid, stream)
-                         : launch_d<false, 64>(p, layout, mask, grid, stream);
+  if (waves_per_item(p) == 8) return launch_nw<8>(p, is_bf16, head_dim, layout, mask, stream);
+  return launch_nw<4>(p, is_bf16, head_dim, layout, mask, stream);
 }
 
 }  // namespace ra

@@ -69,6 +69,13 @@ extern "C" {
 
 const char* ra_last_error(void) { return g_err; }
 
+ra_status ra_set_workgroup_waves(int32_t waves) {
+  if (waves != 0 && waves != 4 && waves != 8)
+    return fail(RA_EINVAL, "waves must be 0 (per launch), 4 or 8, got %d", waves);
+  ra::set_waves_override(waves);
+  return ok();
+}
+
 ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, const void* v,
                        const int32_t* kv_indptr, const int32_t* q_rope_position,
                        const int32_t* mn_indptr, const int32_t* tree_mask, void* out, float* lse,

@@ -6,10 +6,11 @@
 
 namespace ra {
 
-// Packed query rows per work item (4 waves x 32 rows) and keys per KV tile.
-constexpr int kBM = 128;
+// Keys per KV tile, and packed query rows per work item of a four-wave
+// workgroup (4 waves x 32 rows; the split-KV launches use four waves, other
+// launches the count waves_per_item picks).
 constexpr int kBN = 64;
-constexpr int kThreads = 256;
+constexpr int kBM = 128;
 
 enum KvLayout { kContiguous = 0, kPaged = 1 };
 enum MaskKind { kMaskCausal = 0, kMaskTree = 1 };  // kMaskCausal also covers "no mask"
@@ -80,6 +81,11 @@ struct AppendParams {
 };
 
 // Launchers (attn_fwd.hip / kv_append.hip). Return the hipError_t of the launch.
+// Waves per workgroup (4 or 8) that launch_attn uses for p: the work item is
+// 32 packed query rows per wave. set_waves_override(0 | 4 | 8) fixes it for
+// every later launch without split-KV (0: chosen per launch).
+int waves_per_item(const AttnParams& p);
+void set_waves_override(int waves);
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
                        MaskKind mask, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int is_bf16, int head_dim, hipStream_t stream);

@@ -3,7 +3,8 @@
  *
  * C ABI of libragattn.so. Every entry point launches asynchronously on the
  * caller's HIP stream, never synchronises, allocates no device memory and
- * keeps no state between calls. Pointers are caller-owned device memory
+ * keeps no state between calls (apart from the process-wide workgroup shape
+ * that ra_set_workgroup_waves may fix). Pointers are caller-owned device memory
  * unless stated otherwise; inputs are read-only. Index arrays are int32.
  *
  * Operation defined by the TVM pages (cited by page and section):
@@ -223,6 +224,20 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
                              int32_t nnz_pages, int32_t page_size, int32_t h_kv,
                              int32_t head_dim, ra_dtype dtype, float rope_scale,
                              float rope_theta, hipStream_t stream);
+
+/*
+ * Workgroup shape of the attention kernels (a tuning override; results do not
+ * depend on it beyond rounding order, which it leaves unchanged): waves = 4
+ * or 8 fixes 4 or 8 waves of 64 per workgroup, i.e. 128 or 256 packed query
+ * rows (token, head of the group) per work item, for every later
+ * ra_tree_attn, ra_paged_attn and ra_ragged_prefill launch in the process;
+ * waves = 0 (the default) lets each launch choose: 8 when its 256-row work
+ * items cover the GPU's 256 compute units at least twice, else 4. Eight
+ * waves share each K/V tile between twice the rows (half the K/V loads per
+ * row) at one workgroup per compute unit. Split-KV launches always use 4.
+ * Errors: RA_EINVAL for any other value (the setting is then unchanged).
+ */
+ra_status ra_set_workgroup_waves(int32_t waves);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);

@@ -190,3 +190,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         ra.library()
+
+
+def test_set_workgroup_waves_validates(lib):
+    for bad in (-1, 1, 2, 3, 5, 16):
+        assert lib.ra_set_workgroup_waves(bad) == ra.RA_EINVAL
+        assert "waves" in ra.ra_last_error()
+    for good in (4, 8, 0):
+        assert lib.ra_set_workgroup_waves(good) == ra.RA_OK

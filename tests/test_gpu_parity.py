@@ -289,3 +289,53 @@ def test_ragged_left_padded_workload_sampled():
     from workloads import make_extra
     w = make_extra("ragged_left_padded")
     _check(w, w.name, rows=sample_rows(w, per_seq=24, seed=3))
+
+
+# ---------------------------------------------------------------------------
+# the other workgroup shape on the same cases: small cases choose four waves
+# by default and the large workloads eight, so each is rerun with the other
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def waves():
+    import attention_ragged_gqa_amd as ra
+
+    def set_(n):
+        ra.ra_set_workgroup_waves(n)
+    yield set_
+    ra.ra_set_workgroup_waves(0)
+
+
+@pytest.mark.parametrize("case", range(len(TREE_CASES)))
+def test_tree_small_eight_waves(case, waves):
+    waves(8)
+    test_tree_small(case)
+
+
+def test_tree_chain_and_singletons_eight_waves(waves):
+    waves(8)
+    test_tree_chain_and_singletons()
+
+
+@pytest.mark.parametrize("case", range(len(PAGED_CASES)))
+def test_paged_small_eight_waves(case, waves):
+    waves(8)
+    test_paged_small(case)
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED_CASES))
+def test_ragged_prefill_padded_eight_waves(case, waves):
+    waves(8)
+    test_ragged_prefill_padded(case)
+
+
+@pytest.mark.parametrize("k", [0, 1])
+def test_config_parity_full_eight_waves(k, waves):
+    waves(8)
+    test_config_parity_full(k)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_config_parity_sampled_four_waves(k, waves):
+    waves(4)
+    test_config_parity_sampled(k)

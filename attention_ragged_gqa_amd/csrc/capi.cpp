@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "ra_internal.h"
@@ -40,6 +41,20 @@ ra_status check_common(const void* q, const void* q_indptr, const void* out, con
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(RA_EINVAL, "sm_scale must be finite and > 0");
   if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported (fp16=0, bf16=1)", (int)dtype);
   if (head_dim != 64 && head_dim != 128) return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  return RA_OK;
+}
+
+// Size limits of the attention kernels: (token, head) row indices are 32-bit,
+// and the index arrays read through bounds-checked buffer loads address at
+// most 2^31 - 1 bytes (positions and page numbers 4 bytes each, tree entries
+// 8); a sequence's chunk length, up to 16 * its page count, is 32-bit too.
+ra_status check_limits(int32_t total_q, int32_t h_q, int32_t tree_size, int32_t nnz_pages) {
+  if (static_cast<int64_t>(total_q) * h_q > INT32_MAX)
+    return fail(RA_EUNSUPPORTED, "total_q * h_q = %lld exceeds 2^31 - 1",
+                static_cast<long long>(total_q) * h_q);
+  if (total_q >= (1 << 29)) return fail(RA_EUNSUPPORTED, "total_q %d exceeds 2^29 - 1", total_q);
+  if (tree_size >= (1 << 28)) return fail(RA_EUNSUPPORTED, "tree_size %d exceeds 2^28 - 1", tree_size);
+  if (nnz_pages >= (1 << 27)) return fail(RA_EUNSUPPORTED, "nnz_pages %d exceeds 2^27 - 1", nnz_pages);
   return RA_OK;
 }
 
@@ -88,6 +103,7 @@ ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, co
   if (st != RA_OK) return st;
   if ((st = check_rope(rotary_mode, rope_scale, rope_theta)) != RA_OK) return st;
   if (total_kv < 0 || tree_size < 0) return fail(RA_EINVAL, "negative total_kv or tree_size");
+  if ((st = check_limits(total_q, h_q, tree_size, 0)) != RA_OK) return st;
   if (batch > 0 && (kv_indptr == nullptr || mn_indptr == nullptr))
     return fail(RA_EINVAL, "kv_indptr and mn_indptr must be non-NULL");
   if (total_kv > 0 && (k == nullptr || v == nullptr)) return fail(RA_EINVAL, "k and v must be non-NULL");
@@ -174,6 +190,7 @@ static ra_status paged_attn_impl(const void* q, const int32_t* q_indptr, const v
   if ((st = check_rope(rotary_mode, rope_scale, rope_theta)) != RA_OK) return st;
   if (page_size != 16) return fail(RA_EUNSUPPORTED, "page_size %d not supported (16)", page_size);
   if (num_pages < 0 || nnz_pages < 0 || tree_size < 0) return fail(RA_EINVAL, "negative num_pages, nnz_pages or tree_size");
+  if ((st = check_limits(total_q, h_q, tree_size, nnz_pages)) != RA_OK) return st;
   if (sliding_window != 0 && sliding_window != 1) return fail(RA_EINVAL, "sliding_window must be 0 or 1");
   if (batch > 0 && (page_indptr == nullptr || length_info == nullptr))
     return fail(RA_EINVAL, "page_indptr and length_info must be non-NULL");
@@ -273,6 +290,7 @@ ra_status ra_ragged_prefill(const void* q, const int32_t* q_indptr, const void* 
                               sm_scale);
   if (st != RA_OK) return st;
   if (total_kv < 0) return fail(RA_EINVAL, "negative total_kv");
+  if ((st = check_limits(total_q, h_q, 0, 0)) != RA_OK) return st;
   if (batch > 0 && kv_indptr == nullptr) return fail(RA_EINVAL, "kv_indptr is NULL");
   if (total_kv > 0 && (k == nullptr || v == nullptr)) return fail(RA_EINVAL, "k and v must be non-NULL");
   if (pad_mode < 0 || pad_mode > 2) return fail(RA_EINVAL, "pad_mode must be 0, 1 or 2, got %d", pad_mode);

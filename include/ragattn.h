@@ -30,6 +30,9 @@
  *   tree masks [n, 2] rows of (enter, exit): DFS pre-order index and
  *              pre-order index + subtree size of each tree node.
  *
+ * Size limits of the attention entry points (RA_EUNSUPPORTED beyond them):
+ * total_q * h_q < 2^31, total_q < 2^29, tree_size < 2^28, nnz_pages < 2^27.
+ *
  * Index arrays must be consistent with the sizes passed (indptr arrays
  * non-decreasing, entries inside their arrays). The kernels bound every
  * access they derive from them by the sizes given: a row, page or tree entry

@@ -70,6 +70,10 @@ def _tree(lib, **kw):
     (dict(rot=1, null=(5,)), ra.RA_EINVAL),     # q_rope_position
     (dict(d=96), ra.RA_EUNSUPPORTED),
     (dict(dtype=7), ra.RA_EUNSUPPORTED),
+    # size limits: 32-bit (token, head) rows, 2^31-byte index arrays
+    (dict(total_q=1 << 26, total_kv=4, h_q=64, h_kv=8), ra.RA_EUNSUPPORTED),   # total_q * h_q = 2^32
+    (dict(total_q=(1 << 29) + 1, total_kv=4, h_q=2, h_kv=2), ra.RA_EUNSUPPORTED),
+    (dict(tree_size=1 << 28), ra.RA_EUNSUPPORTED),
 ])
 def test_tree_attn_rejects(lib, kw, status):
     assert _tree(lib, **kw) == status
@@ -113,6 +117,8 @@ P_ = ctypes.c_void_p(0x1000)
     (dict(ptrs={"length_info": None}), ra.RA_EINVAL),
     (dict(h_q=12, h_kv=8), ra.RA_EINVAL),
     (dict(d=256), ra.RA_EUNSUPPORTED),
+    (dict(nnz=1 << 27), ra.RA_EUNSUPPORTED),
+    (dict(total_q=(1 << 31) // 8, h_q=8, h_kv=2), ra.RA_EUNSUPPORTED),   # total_q * h_q = 2^31
 ])
 def test_paged_attn_rejects(lib, kw, status):
     assert _paged(lib, **kw) == status

@@ -8,14 +8,17 @@
 // "tree_attn.py" page) and the page gather of that page's paged tree kernel.
 // How it is computed is designed for CDNA4:
 //
-//  * Work item = (sequence, KV head, tile of 128 packed query rows). Packed
+//  * Work item = (sequence, KV head, tile of 32 NW packed query rows, NW = 4
+//    or 8 waves per workgroup). Packed
 //    row R of a sequence is token R / g, query head kvh*g + R % g (g = h_q/h_kv),
 //    so one K/V tile feeds all g heads that share it. Items are enumerated
 //    KV-head-major, then by sequence, with the heaviest tile of each
 //    (sequence, KV head) first, and split into 8 contiguous chunks, one per
 //    XCD (workgroups are handed to XCDs round-robin): the tiles that share
 //    K/V run on one XCD's L2 and every XCD gets the same mix of sequences.
-//  * A workgroup is 4 waves of 64; each wave owns 32 packed rows. Scores are
+//  * A workgroup is NW waves of 64; each wave owns 32 packed rows and loads
+//    64 / NW rows of every K/V tile (eight waves share a tile between twice
+//    the rows, at one workgroup per CU; four run two per CU). Scores are
 //    computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}:
 //    each lane then holds one query row and 16 keys per 32-key block, so row
 //    max and row sum are in-lane plus one v_permlane32_swap, and the fp32
@@ -115,7 +118,7 @@ __device__ __forceinline__ void wait_all_and_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 }
 
-// First token of the 128-row tile starting at packed row row0.
+// First token of the work item starting at packed row row0.
 __device__ __forceinline__ int t_first_of(int row0, int g) { return row0 / g; }
 
 // Locate this workgroup's work item. Returns false when the block has none.

@@ -1,7 +1,7 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
 Small cases are compared element by element on every row; they span several
-128-row query tiles and 64-key KV tiles with ragged tails. The five workloads
+query tiles (128 or 256 packed rows) and 64-key KV tiles with ragged tails. The five workloads
 run at their full sizes in the same launch configuration the benchmark times,
 compared on sampled query tokens (all heads of each), plus properties checked
 on every row.
@@ -170,9 +170,12 @@ def test_deterministic_and_side_stream():
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("n_waves", [0, 8])
+def test_graph_replay_matches_eager(n_waves, waves):
     """The benchmark times HIP-graph replays of the launch: every replay, with
-    eager work and synchronizations in between, must give the eager result."""
+    eager work and synchronizations in between, must give the eager result
+    (with the per-launch workgroup shape, and with eight waves forced)."""
+    waves(n_waves)
     for w in (make_config(1),
               make_custom_paged(32, [130, 9], [300, 40], h_q=16, h_kv=4, d=64, dtype="f16", causal=1)):
         di = DeviceInputs(w)

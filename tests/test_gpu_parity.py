@@ -68,6 +68,8 @@ TREE_CASES = [
     dict(seed=3, sizes=[200], h_q=4, h_kv=4, d=64, dtype="f16", rotary_mode=1, position_offset=5000),
     dict(seed=4, sizes=[17, 90], h_q=16, h_kv=2, d=128, dtype="bf16", rotary_mode=1, rope_theta=5e5),
     dict(seed=5, sizes=[0, 3, 0, 65], h_q=8, h_kv=1, d=128, dtype="f16", rotary_mode=0),
+    # one KV head for all query heads (g = 32: one token per wave)
+    dict(seed=7, sizes=[33, 100], h_q=32, h_kv=1, d=64, dtype="f16", rotary_mode=1),
 ]
 
 
@@ -116,6 +118,11 @@ PAGED_CASES = [
          sliding=([321, 77], [21, 3])),
     dict(seed=23, qo=[5, 129, 64], stored=[777, 1000, 700], h_q=16, h_kv=4, d=128, dtype="bf16", causal=1,
          sliding=([511, 690, 650], [1, 7, 16])),
+    # one KV head for all query heads: a token spans two waves (g = 64) or a
+    # whole four-wave work item (g = 128)
+    dict(seed=24, qo=[3, 70], stored=[500, 260], h_q=64, h_kv=1, d=128, dtype="bf16", causal=1,
+         sliding=([300, 100], [4, 0])),
+    dict(seed=25, qo=[5, 2, 9], stored=[100, 64, 9], h_q=128, h_kv=1, d=64, dtype="f16", causal=1),
 ]
 
 

@@ -31,6 +31,7 @@ __all__ = [
     "ra_merge_states",
     "ra_paged_kv_append",
     "ra_set_workgroup_waves",
+    "ra_attn_workgroup_waves",
     "ra_last_error",
 ]
 
@@ -39,7 +40,7 @@ LIB_NAME = "libragattn.so"
 
 EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
                     "ra_paged_attn_split_workspace", "ra_merge_states", "ra_paged_kv_append",
-                    "ra_set_workgroup_waves", "ra_last_error")
+                    "ra_set_workgroup_waves", "ra_attn_workgroup_waves", "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
 RA_F16, RA_BF16 = 0, 1
@@ -89,6 +90,8 @@ def library() -> ctypes.CDLL:
     lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
     lib.ra_set_workgroup_waves.restype = i32
     lib.ra_set_workgroup_waves.argtypes = [i32]
+    lib.ra_attn_workgroup_waves.restype = i32
+    lib.ra_attn_workgroup_waves.argtypes = [i32] * 4
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_last_error.argtypes = []
     _lib = lib
@@ -107,6 +110,12 @@ def ra_set_workgroup_waves(waves: int) -> None:
     st = library().ra_set_workgroup_waves(int(waves))
     if st != RA_OK:
         raise RagAttnError(st, ra_last_error())
+
+
+def ra_attn_workgroup_waves(total_q: int, h_q: int, h_kv: int, num_kv_splits: int = 1) -> int:
+    """Waves per workgroup (4 or 8) an attention launch of these sizes uses
+    (0 for sizes the entry points reject)."""
+    return int(library().ra_attn_workgroup_waves(int(total_q), int(h_q), int(h_kv), int(num_kv_splits)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

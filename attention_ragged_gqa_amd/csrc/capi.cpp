@@ -91,6 +91,17 @@ ra_status ra_set_workgroup_waves(int32_t waves) {
   return ok();
 }
 
+int32_t ra_attn_workgroup_waves(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits) {
+  if (total_q < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0) return 0;
+  ra::AttnParams p{};
+  p.total_q = total_q;
+  p.h_q = h_q;
+  p.h_kv = h_kv;
+  p.group = h_q / h_kv;
+  p.num_splits = num_kv_splits > 1 ? num_kv_splits : 0;
+  return ra::waves_per_item(p);
+}
+
 ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, const void* v,
                        const int32_t* kv_indptr, const int32_t* q_rope_position,
                        const int32_t* mn_indptr, const int32_t* tree_mask, void* out, float* lse,

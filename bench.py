@@ -273,6 +273,7 @@ def main():
         return
 
     import attention_ragged_gqa_amd as ra
+    import attention_ragged_gqa_amd as ra
     from workloads import EXTRA_NAMES, make_config, make_extra
     from workloads.device import DeviceInputs
 
@@ -380,7 +381,10 @@ def main():
         "fractions": {"mfma": round(mfma_frac, 4), "hbm": round(hbm_frac, 4)},
         "unmasked_pairs": pairs, "roofline": roof,
         "timing": {"mode": "hip_graph_replay" if use_graph else "eager", "launches_per_graph": per_graph,
-                   "eager_ms_per_step": round(ms_eager, 6) if ms_eager is not None else None},
+                   "eager_ms_per_step": round(ms_eager, 6) if ms_eager is not None else None,
+                   # the attention kernel's workgroup shape (split-KV launches: four)
+                   "workgroup_waves": ra.ra_attn_workgroup_waves(
+                       w.total_q, w.h_q, w.h_kv, split if split > 1 else (2 if split == 0 else 1))},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

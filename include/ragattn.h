@@ -242,6 +242,15 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
  */
 ra_status ra_set_workgroup_waves(int32_t waves);
 
+/*
+ * Waves per workgroup (4 or 8) that an attention launch of these sizes uses
+ * under the current ra_set_workgroup_waves setting; num_kv_splits is the
+ * launch's split count (0 or 1: not split). Returns 0 for sizes the entry
+ * points reject (total_q < 0, h_q or h_kv not positive, h_q not a multiple
+ * of h_kv). Launches nothing.
+ */
+int32_t ra_attn_workgroup_waves(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 

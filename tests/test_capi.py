@@ -204,3 +204,25 @@ def test_set_workgroup_waves_validates(lib):
         assert "waves" in ra.ra_last_error()
     for good in (4, 8, 0):
         assert lib.ra_set_workgroup_waves(good) == ra.RA_OK
+
+
+def test_workgroup_waves_policy(lib):
+    """Eight waves when the 256-row items cover the 256 CUs at least twice,
+    four otherwise and for split-KV launches; the override wins; invalid
+    sizes give 0."""
+    q = ra.ra_attn_workgroup_waves
+    assert q(1024, 32, 8) == 4              # 16 trees x 64 nodes: 128 items of 256 rows
+    assert q(11414, 32, 8) == 8             # ragged causal prefill: ~1427 items
+    assert q(32768, 64, 8) == 8             # speculative tree: 8192 items
+    assert q(16, 32, 8) == 4                # decode
+    assert q(32768, 64, 8, 4) == 4          # split-KV
+    assert q(16384, 4, 1) == 4 and q(32768, 4, 1) == 8   # boundary: 256 vs 512 items
+    assert q(10, 6, 4) == 0 and q(-1, 8, 2) == 0 and q(10, 8, 0) == 0
+    try:
+        ra.ra_set_workgroup_waves(8)
+        assert q(1024, 32, 8) == 8 and q(32768, 64, 8, 4) == 4
+        ra.ra_set_workgroup_waves(4)
+        assert q(32768, 64, 8) == 4
+    finally:
+        ra.ra_set_workgroup_waves(0)
+    assert q(32768, 64, 8) == 8

@@ -1110,21 +1110,42 @@ hipError_t launch_nw(const AttnParams& p, int is_bf16, int head_dim, KvLayout la
 
 // Eight-wave workgroups load each K/V tile once for 256 query rows (half the
 // loads per row) but are one per CU, so they pay off only when the 256-row
-// items cover the 256 CUs at least twice; split-KV ranges are short and use
-// four waves. (The item count here ignores ragged tails: a lower bound.)
+// items cover the device's CUs at least twice; split-KV ranges are short and
+// use four waves. (The item count here ignores ragged tails: a lower bound.)
 namespace {
 std::atomic<int> g_waves_override{0};
+
+// Compute units of the current device (256 on a whole MI355X, fewer on a
+// partition of one), queried once per device; 256 when none is visible.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+long current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();   // clear the sticky error state of a failed query
+    return 256;
+  }
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 }  // namespace
 
 void set_waves_override(int waves) { g_waves_override.store(waves, std::memory_order_relaxed); }
 
 int waves_per_item(const AttnParams& p) {
-  constexpr long kCUs = 256;   // MI355X
   if (p.num_splits > 1) return 4;
   const int forced = g_waves_override.load(std::memory_order_relaxed);
   if (forced != 0) return forced;
   const long items8 = (static_cast<long>(p.total_q) * p.group + 255) / 256 * p.h_kv;
-  return items8 >= 2 * kCUs ? 8 : 4;
+  return items8 >= 2 * current_cu_count() ? 8 : 4;
 }
 
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,

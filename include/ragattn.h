@@ -235,7 +235,8 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
  * rows (token, head of the group) per work item, for every later
  * ra_tree_attn, ra_paged_attn and ra_ragged_prefill launch in the process;
  * waves = 0 (the default) lets each launch choose: 8 when its 256-row work
- * items cover the GPU's 256 compute units at least twice, else 4. Eight
+ * items cover the current device's compute units (256 on a whole MI355X)
+ * at least twice, else 4. Eight
  * waves share each K/V tile between twice the rows (half the K/V loads per
  * row) at one workgroup per compute unit. Split-KV launches always use 4.
  * Errors: RA_EINVAL for any other value (the setting is then unchanged).

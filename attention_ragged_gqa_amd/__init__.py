@@ -160,6 +160,61 @@ def _out_lse(q, out, lse):
     return out, lse
 
 
+def _need(cond: bool, msg: str, *args):
+    if not cond:
+        raise ValueError(msg % args if args else msg)
+
+
+def _numel_is(name: str, t, n: int):
+    if t is not None:
+        _need(t.numel() == n, "%s must hold %d entries (got %d)", name, n, t.numel())
+
+
+def _check_qkv(q, k, v):
+    """q [total_q, h_q, d]; k and v [total_kv, h_kv, d] of one shape, h_kv
+    dividing h_q."""
+    _need(q.dim() == 3, "q must be [total_q, h_q, head_dim] (got %d dims)", q.dim())
+    _need(k.dim() == 3 and tuple(k.shape) == tuple(v.shape),
+          "k and v must both be [total_kv, h_kv, head_dim] (got %s and %s)",
+          tuple(k.shape), tuple(v.shape))
+    _need(k.shape[2] == q.shape[2], "k/v head_dim %d != q head_dim %d", k.shape[2], q.shape[2])
+    _need(k.shape[1] > 0 and q.shape[1] % k.shape[1] == 0,
+          "h_q (%d) must be a multiple of h_kv (%d)", q.shape[1], k.shape[1])
+
+
+def _check_indptr(name: str, t, batch: int):
+    _need(t is not None and t.dim() == 1 and t.numel() == batch + 1,
+          "%s must be a [batch + 1] array (batch %d)", name, batch)
+
+
+def _check_paged_shapes(q, q_indptr, pages, page_indptr, length_info, sliding_window,
+                        k_rope_pos_offset, q_rope_position, tree_order_indptr, tree_order):
+    _need(q.dim() == 3, "q must be [total_q, h_q, head_dim] (got %d dims)", q.dim())
+    _need(q_indptr is not None and q_indptr.dim() == 1 and q_indptr.numel() >= 1,
+          "q_indptr must be a [batch + 1] array")
+    batch = q_indptr.numel() - 1
+    _need(pages.dim() == 5 and pages.shape[1] == 2,
+          "pages must be [num_pages, 2, h_kv, page_size, head_dim] (got %s)", tuple(pages.shape))
+    _need(pages.shape[4] == q.shape[2], "pages head_dim %d != q head_dim %d", pages.shape[4], q.shape[2])
+    _need(pages.shape[2] > 0 and q.shape[1] % pages.shape[2] == 0,
+          "h_q (%d) must be a multiple of h_kv (%d)", q.shape[1], pages.shape[2])
+    _check_indptr("page_indptr", page_indptr, batch)
+    _need(length_info is not None, "length_info is required")
+    if sliding_window:
+        _need(tuple(length_info.shape) == (3, batch),
+              "length_info must be [3, batch] with a sliding window (got %s)", tuple(length_info.shape))
+    else:
+        _need(length_info.numel() == batch, "length_info must hold batch (%d) entries", batch)
+    _numel_is("k_rope_pos_offset", k_rope_pos_offset, batch)
+    _numel_is("q_rope_position", q_rope_position, q.shape[0])
+    if tree_order is not None or tree_order_indptr is not None:
+        _need(tree_order_indptr is not None, "tree_order given without tree_order_indptr")
+        _check_indptr("tree_order_indptr", tree_order_indptr, batch)
+        _need(tree_order is not None and tree_order.dim() == 2 and tree_order.shape[1] == 2,
+              "tree_order must be [n, 2]")
+    return batch
+
+
 def ra_tree_attn(q, q_indptr, k, v, kv_indptr, q_rope_position, mn_indptr, tree_mask,
                  out=None, lse=None, rotary_mode: int = 0, rope_scale: float = 1.0,
                  rope_theta: float = 1e4, sm_scale: Optional[float] = None, stream=None):
@@ -168,6 +223,18 @@ def ra_tree_attn(q, q_indptr, k, v, kv_indptr, q_rope_position, mn_indptr, tree_
     q [total_q, h_q, d], k/v [total_kv, h_kv, d] (fp16/bf16); q_indptr,
     kv_indptr, mn_indptr [b+1], q_rope_position [total_q] (or None when
     rotary_mode == 0), tree_mask [n, 2] int32. Returns (out, lse)."""
+    # shapes first: a mismatch must never reach the kernels
+    _check_qkv(q, k, v)
+    _need(q_indptr is not None and q_indptr.dim() == 1 and q_indptr.numel() >= 1,
+          "q_indptr must be a [batch + 1] array")
+    batch = q_indptr.numel() - 1
+    _check_indptr("kv_indptr", kv_indptr, batch)
+    _check_indptr("mn_indptr", mn_indptr, batch)
+    _need(tree_mask is not None and tree_mask.dim() == 2 and tree_mask.shape[1] == 2,
+          "tree_mask must be [n, 2]")
+    if rotary_mode == 1:
+        _need(q_rope_position is not None, "rotary_mode 1 needs q_rope_position")
+    _numel_is("q_rope_position", q_rope_position, q.shape[0])
     dev = q.device
     i32 = torch.int32
     _check_dev("q", q, None, dev)
@@ -201,6 +268,10 @@ def ra_paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info,
 
     pages [num_pages, 2, h_kv, 16, d]; length_info [b] or [3, b] int32.
     Returns (out, lse)."""
+    _check_paged_shapes(q, q_indptr, pages, page_indptr, length_info, sliding_window,
+                        k_rope_pos_offset, q_rope_position, tree_order_indptr, tree_order)
+    if rotary_mode == 1:
+        _need(q_rope_position is not None, "rotary_mode 1 needs q_rope_position")
     dev = q.device
     i32 = torch.int32
     _check_dev("q", q, None, dev)
@@ -240,6 +311,14 @@ def ra_ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len=None, pad_mode: in
     (C: ra_ragged_prefill). q [total_q, h_q, d], k/v [total_kv, h_kv, d];
     pad_mode 0 plain (causal or not), 1 right padding (non-causal),
     2 left padding (causal) with valid_len [b]. Returns (out, lse)."""
+    _check_qkv(q, k, v)
+    _need(q_indptr is not None and q_indptr.dim() == 1 and q_indptr.numel() >= 1,
+          "q_indptr must be a [batch + 1] array")
+    batch = q_indptr.numel() - 1
+    _check_indptr("kv_indptr", kv_indptr, batch)
+    if pad_mode != 0:
+        _need(valid_len is not None, "pad_mode %d needs valid_len", pad_mode)
+    _numel_is("valid_len", valid_len, batch)
     dev = q.device
     i32 = torch.int32
     _check_dev("q", q, None, dev)
@@ -277,6 +356,10 @@ def ra_paged_attn_split(q, q_indptr, pages, page_indptr, page_values, length_inf
     ra_paged_attn, plus num_kv_splits (0: the library chooses) and an optional
     uint8 device workspace; when it is None one is allocated here for the
     largest split count (64). Returns (out, lse)."""
+    _check_paged_shapes(q, q_indptr, pages, page_indptr, length_info, sliding_window,
+                        k_rope_pos_offset, q_rope_position, tree_order_indptr, tree_order)
+    if rotary_mode == 1:
+        _need(q_rope_position is not None, "rotary_mode 1 needs q_rope_position")
     dev = q.device
     i32 = torch.int32
     _check_dev("q", q, None, dev)
@@ -340,6 +423,18 @@ def ra_paged_kv_append(k, v, append_indptr, append_start, rope_position, page_in
                        stream=None):
     """Write tokens k/v [n, h_kv, d] into ``pages`` in place, rotating K at
     rope_position when it is given (C: ra_paged_kv_append)."""
+    _need(pages.dim() == 5 and pages.shape[1] == 2,
+          "pages must be [num_pages, 2, h_kv, page_size, head_dim] (got %s)", tuple(pages.shape))
+    _need(k.dim() == 3 and tuple(k.shape) == tuple(v.shape)
+          and tuple(k.shape[1:]) == (pages.shape[2], pages.shape[4]),
+          "k and v must both be [n_tokens, h_kv, head_dim] = [n, %d, %d] (got %s and %s)",
+          pages.shape[2], pages.shape[4], tuple(k.shape), tuple(v.shape))
+    _need(append_indptr is not None and append_indptr.dim() == 1 and append_indptr.numel() >= 1,
+          "append_indptr must be a [batch + 1] array")
+    batch = append_indptr.numel() - 1
+    _numel_is("append_start", append_start, batch)
+    _check_indptr("page_indptr", page_indptr, batch)
+    _numel_is("rope_position", rope_position, k.shape[0])
     dev = pages.device
     i32 = torch.int32
     _check_dev("pages", pages, None, dev)

@@ -1,19 +1,24 @@
 """Benchmark: ragged, batched, masked GQA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k|name] [--split S]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--copies N] [--no-per-config] [--no-cpu-baseline] [--copy-calibration]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 one launch of the attention kernel (work partition, Q load + RoPE, K/V gather
 + RoPE, QK^T, mask, online softmax, PV, epilogue all run inside it). Inputs
-are resident in HBM before the timed region. Default workload: the batched
-tree-attention configuration (16 trees of 64 nodes, h_q 32 / h_kv 8, d 128,
-fp16, inline RoPE theta 1e4). Other workloads (--config 0..4) print the same
-line for that workload; `--config paged_decode` times the split-KV entry point
-(ra_paged_attn_split, one step = the attention kernel + the merge kernel) on a
-decode batch, `--split S` picks its split count (0: chosen by the library,
--1: the unsplit entry point); `--config ragged_left_padded` times
-ra_ragged_prefill on left-padded causal prompts.
+are resident in HBM before the timed region.
+
+Default workload (the headline): the largest single-GPU configuration, the
+speculative-decode tree over a paged prefix (128 sequences, 4096-token
+prefix + 256-node tree, h_q 64 / h_kv 8, d 128, bf16, q RoPE inline at
+prefix + depth, theta 5e5). The same JSON line carries a ``per_config``
+block timing the other four configurations (tree_tiny, tree_batched,
+paged_causal, paged_sliding) in the same run. ``--config 0..4`` puts another
+configuration in the headline; ``--config paged_decode`` times the split-KV
+entry point (ra_paged_attn_split, one step = the attention kernel + the
+merge kernel) on a decode batch, ``--split S`` picks its split count (0:
+chosen by the library, -1: the unsplit entry point); ``--config
+ragged_left_padded`` times ra_ragged_prefill on left-padded causal prompts.
 
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
@@ -24,10 +29,18 @@ the graph only removes the per-call host cost, which for small workloads is
 comparable to the kernel itself); the duration per step comes from HIP events
 recorded around the replays on the stream the kernels run on. The same
 number of eager launches is timed first and reported as
-timing.eager_ms_per_step. ``roofline.traffic`` is the HBM traffic per
-launch measured by rocprofv3 counters (profiles/<kernel>_<workload>_pmc.md),
-reported only while the kernel source is unchanged since that measurement.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the workload.
+timing.eager_ms_per_step.
+
+HBM-bound workloads (flop/byte below the ridge point) are timed cold: the
+graph cycles through enough separate copies of the inputs (--copies, default
+enough for 512 MiB, twice the 256 MB Infinity Cache) that every launch reads
+its bytes from HBM; the same launch on one resident copy is reported as
+``warm``. ``roofline.traffic`` is the HBM traffic per launch measured by
+rocprofv3 counters (profiles/<kernel>_<workload>_pmc.md), reported only while
+the kernel source is unchanged since that measurement. ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the headline workload: whole passes of
+a small workload, else whole sequences (every row and head of each), with the
+unmasked pairs of exactly those sequences counted.
 """
 
 from __future__ import annotations
@@ -52,7 +65,10 @@ PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense fp16/bf16
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", "attn_fwd.hip")
 KERNEL_NAME = "attn_fwd_kernel"
-DEFAULT_CONFIG = 1
+DEFAULT_CONFIG = 4                 # spec_tree_paged, the largest configuration
+COLD_FOOTPRINT = 512 << 20         # bytes of distinct inputs cycled per graph (HBM-bound)
+# steps per configuration in the per_config block (about 25-100 ms of GPU time each)
+PER_CONFIG_STEPS = {0: 2000, 1: 2000, 2: 200, 3: 200, 4: 20}
 
 
 def log(*a):
@@ -74,15 +90,16 @@ def chunk_lengths(w) -> np.ndarray:
     return stored - li[1].astype(np.int64) + li[2].astype(np.int64)
 
 
-def visible_pairs(w) -> int:
-    """Unmasked (query row, query head, key) triples. Trees: a node sees its
-    depth+1 ancestors-or-self plus the whole prefix; causal: row t of qo sees
+def visible_pairs(w, seqs=None) -> int:
+    """Unmasked (query row, query head, key) triples (of the sequences in
+    ``seqs`` only, when given). Trees: a node sees its depth+1
+    ancestors-or-self plus the whole prefix; causal: row t of qo sees
     min(L, L - qo + t + 1) columns of an L-column chunk; padded batches
     restrict rows and columns to the valid prefix (right) or suffix (left)."""
     L = chunk_lengths(w)
     qo = np.diff(w.q_indptr).astype(np.int64)
     total = 0
-    for b in range(w.batch):
+    for b in (range(w.batch) if seqs is None else seqs):
         if qo[b] == 0:
             continue
         if w.kind == "ragged" and w.pad_mode != 0:
@@ -184,39 +201,47 @@ def measured_traffic(workload: str):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
+    """The CPU oracle as it stands, timed on this host: whole passes of a
+    small workload, or whole sequences of a large one (in order, until the
+    budget is spent), each with the unmasked pairs it actually computes. The
+    page pool the oracle reads is built before the clock starts."""
     from tests.parity import run_oracle
+    from workloads import pages_from_logical
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    pool = pages_from_logical(w) if w.kind == "paged" else None
     if w.total_q * w.h_q <= 64 * 1024:
-        # small workload: whole passes until the budget is spent
         n, t0 = 0, time.perf_counter()
         while True:
-            run_oracle(w)
+            run_oracle(w, pool=pool)
             n += 1
             el = time.perf_counter() - t0
             if el >= budget_s or n >= 50:
                 break
         pairs, sample = pairs_per_pass * n, "%d full passes of the workload" % n
     else:
-        # large workload: the first query token of each sequence, then more
-        # tokens per sequence until the budget is spent; pairs are counted on
-        # the sampled rows only
-        from tests.parity import sample_rows
-        rows = sample_rows(w, per_seq=2, seed=0)
-        frac = len(rows) / max(w.total_q, 1)
-        t0 = time.perf_counter()
-        run_oracle(w, rows=rows)
-        el = time.perf_counter() - t0
-        pairs = int(pairs_per_pass * frac)
-        sample = "%d sampled query tokens (all heads), %.3f%% of the rows; pairs scaled by the row fraction" % (
-            len(rows), 100 * frac)
+        el, pairs, done = 0.0, 0, 0
+        for b in range(w.batch):
+            rows = np.arange(int(w.q_indptr[b]), int(w.q_indptr[b + 1]))
+            if len(rows) == 0:
+                continue
+            t0 = time.perf_counter()
+            run_oracle(w, rows=rows, pool=pool)
+            el += time.perf_counter() - t0
+            pairs += visible_pairs(w, seqs=[b])
+            done += 1
+            if el >= budget_s:
+                break
+        sample = ("sequences 0..%d of %d (every query row and head of each, %.2f%% of the "
+                  "workload's unmasked pairs), pairs counted exactly" % (done - 1, w.batch,
+                                                                        100.0 * pairs / pairs_per_pass))
     tflops = 4.0 * w.d * pairs / el / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(el, 3),
+            "sample": sample, "seconds": round(el, 3), "estimated": False,
             "cpu": _cpu_model()}
 
 
@@ -231,6 +256,8 @@ def _cpu_model() -> str:
 
 
 # ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
 
 def copy_calibration(steps: int):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
@@ -244,16 +271,128 @@ def copy_calibration(steps: int):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps}))
 
 
+def bound_of(w) -> str:
+    """'mfma' when the workload's flop/byte ratio is above the ridge point."""
+    ai = 4.0 * w.d * visible_pairs(w) / algorithmic_bytes(w)
+    return "mfma" if ai > PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+
+
+def time_steps(dis, steps: int, warmup: int, graph_launches: int, launch_kw: dict,
+               eager_steps: int):
+    """Warm up, time `eager_steps` eager launches, then time exactly `steps`
+    launches as HIP-graph replays (graph_launches per graph; 0: eager). Launch
+    i uses dis[i % len(dis)]. Returns (ms per step, eager ms per step or None,
+    launches per graph)."""
+    import torch
+    n = len(dis)
+    for i in range(warmup):
+        dis[i % n].launch(**launch_kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()       # the stream the kernels are launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ms_eager = None
+    if eager_steps > 0:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(eager_steps):
+            dis[i % n].launch(**launch_kw)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_eager = ev0.elapsed_time(ev1) / eager_steps
+
+    use_graph = graph_launches > 0
+    per_graph = max(1, min(steps, graph_launches)) if use_graph else 0
+    reps, rem = divmod(steps, per_graph) if use_graph else (0, 0)
+
+    def capture(count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                dis[i % n].launch(**launch_kw)
+        return g
+
+    if use_graph:
+        g_main = capture(per_graph)
+        g_rem = capture(rem) if rem else None
+        g_main.replay()
+        torch.cuda.synchronize()
+    ev0.record(stream)
+    if use_graph:
+        for _ in range(reps):
+            g_main.replay()
+        if g_rem is not None:
+            g_rem.replay()
+    else:
+        for i in range(steps):
+            dis[i % n].launch(**launch_kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, ms_eager, per_graph
+
+
+def rates(w, ms_step: float) -> dict:
+    """Throughput and roofline fractions of one step of w taking ms_step."""
+    pairs = visible_pairs(w)
+    flops = 4.0 * w.d * pairs
+    nbytes = algorithmic_bytes(w)
+    t_s = ms_step / 1e3
+    tflops = flops / t_s / 1e12
+    gbs = nbytes / t_s / 1e9
+    return {"ms_per_step": round(ms_step, 6), "tflops": round(tflops, 3),
+            "tokens_per_s": round(w.total_q / t_s, 1), "gbs": round(gbs, 2),
+            "mfma_frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "pairs": pairs, "flops": flops, "bytes": nbytes}
+
+
+def measure(w, steps, warmup, graph_launches, launch_kw, eager_steps, copies=None):
+    """Time w. HBM-bound workloads are timed cold, cycling through `copies`
+    (default: COLD_FOOTPRINT worth) separate input copies, and warm on one
+    copy; others warm only. Returns (result dict, copies used)."""
+    from workloads.device import DeviceInputs
+    bound = bound_of(w)
+    di = DeviceInputs(w, "cuda:0")
+    if copies is None:
+        copies = 1 if bound == "mfma" else max(1, min(64, -(-COLD_FOOTPRINT // algorithmic_bytes(w))))
+    ms_warm, ms_eager, per_graph = time_steps([di], steps, warmup, graph_launches, launch_kw, eager_steps)
+    res = {"bound": bound, "copies": copies, "eager_ms_per_step": ms_eager, "launches_per_graph": per_graph}
+    if copies > 1:
+        dis = [di] + [DeviceInputs(w, "cuda:0") for _ in range(copies - 1)]
+        ms_cold, _, per_graph = time_steps(dis, steps, warmup, graph_launches, launch_kw, 0)
+        res.update(rates(w, ms_cold))
+        res["warm"] = rates(w, ms_warm)
+        del dis
+    else:
+        res.update(rates(w, ms_warm))
+    res["frac"] = res["mfma_frac"] if bound == "mfma" else res["hbm_frac"]
+    return res, copies
+
+
+def per_config_entry(w, r) -> dict:
+    e = {"workload": w.name, "dtype": w.dtype, "bound": r["bound"], "frac": r["frac"],
+         "ms_per_step": r["ms_per_step"], "tflops": r["tflops"], "tokens_per_s": r["tokens_per_s"],
+         "mfma_frac": r["mfma_frac"], "hbm_frac": r["hbm_frac"],
+         "timing": "cold (%d input copies cycled)" % r["copies"] if r["copies"] > 1 else "warm"}
+    if "warm" in r:
+        e["warm"] = {k: r["warm"][k] for k in ("ms_per_step", "tflops", "hbm_frac", "mfma_frac")}
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=str(DEFAULT_CONFIG),
                     help="0..4, or an extra workload name (paged_decode, ragged_left_padded)")
     ap.add_argument("--split", type=int, default=None,
                     help="split-KV count for paged workloads (0: auto, -1: unsplit entry point); "
                          "default: auto for paged_decode, unsplit otherwise")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="input copies cycled per graph (default: 1 for MFMA-bound workloads, "
+                         "512 MiB worth for HBM-bound ones)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graph-launches", type=int, default=100,
@@ -273,9 +412,7 @@ def main():
         return
 
     import attention_ragged_gqa_amd as ra
-    import attention_ragged_gqa_amd as ra
-    from workloads import EXTRA_NAMES, make_config, make_extra
-    from workloads.device import DeviceInputs
+    from workloads import CONFIG_NAMES, EXTRA_NAMES, make_config, make_extra
 
     ra.library()
     t_gen = time.perf_counter()
@@ -287,108 +424,65 @@ def main():
         split = -1
     launch_kw = {} if split < 0 else {"num_kv_splits": split}
     log("[bench] generated %s in %.1fs" % (w.name, time.perf_counter() - t_gen))
-    di = DeviceInputs(w, "cuda:0")
-    torch.cuda.synchronize()
-    log("[bench] inputs resident on cuda:0")
-
-    for _ in range(args.warmup):
-        di.launch(**launch_kw)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()       # the stream the kernel is launched on
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-
-    # Eager launches, one Python call each: for small workloads the host
-    # issue rate (ctypes + hipLaunchKernel) can be the bound, so this is
-    # reported alongside and the steps are timed as HIP graph replays.
     eager_steps = args.steps if args.eager_steps is None else args.eager_steps
-    ms_eager = None
-    if eager_steps > 0:
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(eager_steps):
-            di.launch(**launch_kw)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms_eager = ev0.elapsed_time(ev1) / eager_steps
-
-    use_graph = args.graph_launches > 0
-    per_graph = max(1, min(args.steps, args.graph_launches)) if use_graph else 0
-    reps, rem = divmod(args.steps, per_graph) if use_graph else (0, 0)
-
-    def capture(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(n):
-                di.launch(**launch_kw)
-        return g
-
-    if use_graph:
-        g_main = capture(per_graph)
-        g_rem = capture(rem) if rem else None
-        g_main.replay()
-        torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    if use_graph:
-        for _ in range(reps):
-            g_main.replay()
-        if g_rem is not None:
-            g_rem.replay()
-    else:   # eager launches only (--graph-launches 0)
-        for _ in range(args.steps):
-            di.launch(**launch_kw)
-    ev1.record(stream)
+    r, copies = measure(w, args.steps, args.warmup, args.graph_launches, launch_kw, eager_steps,
+                        args.copies)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    log("[bench] %d steps as graph replays (%d launches per graph): %.3f ms (events), %.3f s wall;"
-        " eager %s ms/step" % (args.steps, per_graph, ms_total, wall,
-                               "%.5f" % ms_eager if ms_eager is not None else "-"))
+    log("[bench] %s: %d steps, %.5f ms/step (%s)" % (w.name, args.steps, r["ms_per_step"],
+                                                     "cold, %d copies" % copies if copies > 1 else "warm"))
 
-    pairs = visible_pairs(w)
-    flops = 4.0 * w.d * pairs
-    nbytes = algorithmic_bytes(w)
-    t_s = ms_step / 1e3
-    tflops = flops / t_s / 1e12
-    gbs = nbytes / t_s / 1e9
-    tokens_s = w.total_q / t_s
-    hbm_frac = gbs / PEAK_HBM_GBS
-    mfma_frac = tflops / PEAK_MFMA_TFLOPS
-    ai = flops / nbytes
-    bound = "mfma" if ai > PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
+    bound = r["bound"]
     if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(hbm_frac, 4)}
+        roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": r["hbm_frac"]}
     else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+        roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": r["mfma_frac"]}
     roof["traffic"] = measured_traffic(w.name)
-    roof["algorithmic_bytes"] = nbytes
-    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = r["bytes"]
+    roof["algorithmic_flops"] = r["flops"]
     roof["kernel"] = KERNEL_NAME
 
     line = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if w.dtype == "f16" else "bf16", "data": "synthetic",
         "config": dict(config_summary(w), **({"kv_splits": "auto" if split == 0 else split}
                                                if split >= 0 else {})),
-        "tokens_per_s": round(tokens_s, 1),
-        "fractions": {"mfma": round(mfma_frac, 4), "hbm": round(hbm_frac, 4)},
-        "unmasked_pairs": pairs, "roofline": roof,
-        "timing": {"mode": "hip_graph_replay" if use_graph else "eager", "launches_per_graph": per_graph,
-                   "eager_ms_per_step": round(ms_eager, 6) if ms_eager is not None else None,
+        "tokens_per_s": r["tokens_per_s"],
+        "fractions": {"mfma": r["mfma_frac"], "hbm": r["hbm_frac"]},
+        "unmasked_pairs": r["pairs"], "roofline": roof,
+        "timing": {"mode": "hip_graph_replay" if args.graph_launches > 0 else "eager",
+                   "launches_per_graph": r["launches_per_graph"],
+                   "input_copies": copies,
+                   "eager_ms_per_step": round(r["eager_ms_per_step"], 6) if r["eager_ms_per_step"] is not None else None,
                    # the attention kernel's workgroup shape (split-KV launches: four)
                    "workgroup_waves": ra.ra_attn_workgroup_waves(
                        w.total_q, w.h_q, w.h_kv, split if split > 1 else (2 if split == 0 else 1))},
     }
+    if "warm" in r:
+        line["warm"] = r["warm"]
+
+    if not args.no_per_config:
+        per = [per_config_entry(w, r)] if args.config in [str(k) for k in range(len(CONFIG_NAMES))] else []
+        for k in range(len(CONFIG_NAMES)):
+            if str(k) == args.config:
+                continue
+            t0 = time.perf_counter()
+            wk = make_config(k)
+            rk, _ = measure(wk, PER_CONFIG_STEPS[k], 5, args.graph_launches, {}, 0)
+            per.append(per_config_entry(wk, rk))
+            log("[bench] per-config %s: %.5f ms/step, %s frac %.4f (%.1fs)"
+                % (wk.name, rk["ms_per_step"], rk["bound"], rk["frac"], time.perf_counter() - t0))
+            del wk
+            torch.cuda.empty_cache()
+        per.sort(key=lambda e: CONFIG_NAMES.index(e["workload"]) if e["workload"] in CONFIG_NAMES else 99)
+        line["per_config"] = per
+
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(w, pairs)
+        line["cpu_baseline"] = cpu_baseline(w, r["pairs"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

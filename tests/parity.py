@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from workloads import pages_from_logical
-from workloads.device import DeviceInputs, gpu_pages  # noqa: F401
+from workloads.device import DeviceInputs, append_range, gpu_pages  # noqa: F401
 
 OUT_ATOL = 1e-2
 OUT_ARITH = 2e-3
@@ -41,7 +41,10 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_oracle(w, rows=None):
+def run_oracle(w, rows=None, pool=None):
+    """The oracle on workload w (rows: global query tokens to evaluate, all
+    when None). pool: the page pool of a paged workload as
+    pages_from_logical(w) returns it, when the caller has built it already."""
     if w.kind == "ragged":
         return oracle.ragged_prefill(w.q, w.q_indptr, w.k, w.v, w.kv_indptr, w.valid_len,
                                      w.pad_mode, w.causal, w.sm_scale, rows=rows)
@@ -55,7 +58,9 @@ def run_oracle(w, rows=None):
               rows=rows)
     if w.store_rope_position is not None:
         kw.update(cache_rope_position=w.store_rope_position, cache_rope_indptr=w.kv_store_indptr)
-    return oracle.paged_attn(w.q, w.q_indptr, pages_from_logical(w), w.page_indptr, w.page_values,
+    if pool is None:
+        pool = pages_from_logical(w)
+    return oracle.paged_attn(w.q, w.q_indptr, pool, w.page_indptr, w.page_values,
                              w.length_info, w.sliding_window, w.causal, w.sm_scale, w.dtype, **kw)
 
 

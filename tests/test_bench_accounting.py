@@ -77,3 +77,25 @@ def test_out_tolerance_only_relaxes_where_dtype_cannot_hold_1e2():
     assert np.all(out_tolerance(np.array([0.0, 5.0, 31.0]), hf) == 1e-2)
     assert abs(out_tolerance(np.array([5.0]), bf)[0] - (2.0 ** -6 + 2e-3)) < 1e-12
     assert abs(out_tolerance(np.array([-9.0]), bf)[0] - (2.0 ** -5 + 2e-3)) < 1e-12
+
+
+def test_visible_pairs_per_sequence_sum_to_total():
+    for w in (make_config(1), make_custom_paged(9, [7, 40, 0, 3], [30, 40, 5, 80], h_q=4, h_kv=1, d=64,
+                                                dtype="bf16", causal=1)):
+        assert sum(bench.visible_pairs(w, seqs=[b]) for b in range(w.batch)) == bench.visible_pairs(w)
+
+
+def test_cpu_baseline_counts_what_it_times():
+    w = make_config(0)
+    r = bench.cpu_baseline(w, bench.visible_pairs(w), budget_s=0.2)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert r["estimated"] is False
+    w = make_custom_paged(10, [300, 200, 100], [400, 200, 900], h_q=128, h_kv=8, d=64, dtype="bf16",
+                          causal=1)
+    r = bench.cpu_baseline(w, bench.visible_pairs(w), budget_s=0.01)
+    assert r["sample"].startswith("sequences 0..0 of 3")   # one whole sequence, then the budget is spent
+
+
+def test_bound_of_configs():
+    assert bench.bound_of(make_config(1)) == "hbm"
+    assert bench.bound_of(make_config(2)) == "mfma"

@@ -18,18 +18,41 @@ def _i32(a, dev):
     return None if a is None else torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
 
 
+def append_range(pool, w, starts, lens, dev):
+    """Append tokens [starts[b], starts[b] + lens[b]) of each sequence's
+    stored tokens into ``pool`` with the library's append kernel, at storage
+    offsets starts[b] (any offset: mid-page starts are the normal case),
+    rotating K at the workload's cache positions."""
+    import attention_ragged_gqa_amd as ra
+    starts = np.asarray(starts, np.int64)
+    lens = np.asarray(lens, np.int64)
+    idx = np.concatenate([np.arange(int(w.kv_store_indptr[b]) + starts[b],
+                                    int(w.kv_store_indptr[b]) + starts[b] + lens[b])
+                          for b in range(w.batch)]).astype(np.int64) if w.batch else np.zeros(0, np.int64)
+    sel = torch.from_numpy(idx)
+    indptr = np.zeros(w.batch + 1, np.int64)
+    indptr[1:] = np.cumsum(lens)
+    ra.ra_paged_kv_append(w.k_store[sel].to(dev), w.v_store[sel].to(dev), _i32(indptr, dev),
+                          _i32(starts, dev), _i32(np.asarray(w.store_rope_position)[idx], dev),
+                          _i32(w.page_indptr, dev), _i32(w.page_values, dev), pool,
+                          rope_scale=w.rope_scale, rope_theta=w.rope_theta)
+
+
 def gpu_pages(w, dev):
     """Page pool on the device. K rotated before caching is written by the
-    library's append kernel; otherwise the generator's pages are copied."""
-    import attention_ragged_gqa_amd as ra
+    library's append kernel in two calls, as a cache is filled in use: each
+    sequence's cached prefix at storage offset 0, then its new tokens (the
+    last qo_len stored tokens, the ones the queries belong to) appended
+    after it, usually starting mid-page. Otherwise the generator's pages are
+    copied."""
     if w.store_rope_position is None:
         return pages_from_logical(w).to(dev)
     pool = torch.zeros((w.num_pages, 2, w.h_kv, 16, w.d), dtype=w.q.dtype, device=dev)
-    ra.ra_paged_kv_append(w.k_store.to(dev), w.v_store.to(dev), _i32(w.kv_store_indptr, dev),
-                          torch.zeros(w.batch, dtype=torch.int32, device=dev),
-                          _i32(w.store_rope_position, dev), _i32(w.page_indptr, dev),
-                          _i32(w.page_values, dev), pool, rope_scale=w.rope_scale,
-                          rope_theta=w.rope_theta)
+    stored = np.diff(w.kv_store_indptr).astype(np.int64)
+    new = np.minimum(np.diff(w.q_indptr).astype(np.int64), stored)
+    old = stored - new
+    append_range(pool, w, np.zeros(w.batch, np.int64), old, dev)
+    append_range(pool, w, old, new, dev)
     return pool
 
 
@@ -44,8 +67,9 @@ class DeviceInputs:
         self.q = w.q.to(d)
         self.q_indptr = _i32(w.q_indptr, d)
         self.q_rope_position = _i32(w.q_rope_position, d) if w.rotary_mode == 1 else None
-        self.out = torch.empty_like(self.q)
-        self.lse = torch.empty(w.total_q, w.h_q, dtype=torch.float32, device=d)
+        # poisoned: a row the kernels never write stays NaN
+        self.out = torch.full_like(self.q, float("nan"))
+        self.lse = torch.full((w.total_q, w.h_q), float("nan"), dtype=torch.float32, device=d)
         if w.kind == "tree":
             self.k = w.k.to(d)
             self.v = w.v.to(d)
@@ -65,6 +89,12 @@ class DeviceInputs:
             self.k_rope_pos_offset = _i32(w.k_rope_pos_offset, d)
             self.tree_order_indptr = _i32(w.tree_order_indptr, d)
             self.tree_order = _i32(None if w.tree_order is None else w.tree_order.reshape(-1, 2), d)
+
+    def poison(self):
+        """Fill out and lse with NaN, so that rows a launch leaves unwritten
+        are caught by the finiteness checks."""
+        self.out.fill_(float("nan"))
+        self.lse.fill_(float("nan"))
 
     def launch(self, stream=None, num_kv_splits=None):
         """One launch; num_kv_splits (paged only) selects the split-KV entry

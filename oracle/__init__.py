@@ -16,8 +16,8 @@ rounded to the storage dtype.
 
 Modules:
   attention -- vectorised float64 oracle (tree_attn, paged_attn,
-               ragged_prefill with padded masks, rope, masks, merge_states
-               for split key sets)
+               ragged_prefill with padded masks, mla_paged_attn over a
+               latent cache, rope, masks, merge_states for split key sets)
   scalar    -- pure-Python brute force for tiny inputs (ancestor sets from
                parent pointers rather than DFS intervals)
 """
@@ -28,6 +28,7 @@ from .attention import (  # noqa: F401
     causal_visible,
     kv_chunk_len,
     merge_states,
+    mla_paged_attn,
     padded_visible,
     paged_attn,
     ragged_prefill,

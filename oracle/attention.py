@@ -168,10 +168,11 @@ def seq_offset(j: np.ndarray, b: int, length_info, sliding_window: int) -> np.nd
 def attend(qr: np.ndarray, kr: np.ndarray, vr: np.ndarray, vis: np.ndarray, sm_scale: float):
     """out = softmax(sm_scale * q k^T | visible) v and lse = log2 sum exp.
 
-    qr [R, D], kr [L, D], vr [L, D] float64; vis [R, L] bool.
+    qr [R, D], kr [L, D], vr [L, Dv] float64 (Dv = D, or the latent width
+    for multi-head latent attention); vis [R, L] bool.
     Rows with no visible key: out = 0, lse = -inf."""
-    R, D = qr.shape
-    out = np.zeros((R, D), dtype=np.float64)
+    R = qr.shape[0]
+    out = np.zeros((R, vr.shape[1]), dtype=np.float64)
     lse = np.full(R, -np.inf, dtype=np.float64)
     if kr.shape[0] == 0 or R == 0:
         return out, lse
@@ -390,4 +391,53 @@ def ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len, pad_mode: int, causa
         tok = q0 + qi
         _attend_sequence(_f64(q[tok]), tok, qi, _f64(k[k0:k1]), _f64(v[k0:k1]), vis, h_q, h_kv,
                          sm_scale, out, lse)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# multi-head latent attention over a paged latent cache
+# ----------------------------------------------------------------------------
+
+def mla_paged_attn(q, q_indptr, pages, page_indptr, page_values, last_page_len, causal: int,
+                   sm_scale: float, d_latent: int, rows: Optional[np.ndarray] = None):
+    """Multi-head latent attention prefill ("_kernel_common.py" page: AttnKind
+    MLA, and _alloc_mla_qkvo_buffers, whose one combined KV tile serves as K
+    over all d_qk columns and as V over the first d_latent columns; the
+    epilogue paged_store_output_lse with every query head in one group).
+
+    q [total_q, h_q, d_qk]; pages [num_pages, 16, d_qk] hold one latent row
+    per token (no K/V split, no KV heads); sequence b's rows are at storage
+    offsets 0..kv_len-1, kv_len = (np - 1) * 16 + last_page_len[b] for its
+    np pages (0 with no pages), offset o in page page_values[page_indptr[b]
+    + o // 16], slot o % 16. For query token i of sequence b and head h:
+      s_j = sm_scale * sum_{t < d_qk} q[i, h, t] kv_j[t]
+      out[i, h, :] = sum_j softmax(s)_j kv_j[:d_latent]
+      lse[i, h] = log2 sum_j exp(s_j)
+    over the keys the causal test (_causal_mask) leaves visible.
+    Returns (out [total_q, h_q, d_latent], lse [total_q, h_q]) float64."""
+    total_q, h_q, d_qk = q.shape
+    out = np.full((total_q, h_q, d_latent), np.nan)
+    lse = np.full((total_q, h_q), np.nan)
+    q_indptr = np.asarray(q_indptr)
+    page_indptr = np.asarray(page_indptr)
+    page_values = np.asarray(page_values)
+    for b in range(len(q_indptr) - 1):
+        qi = _select_tokens(q_indptr, rows, b)
+        if len(qi) == 0:
+            continue
+        q0 = int(q_indptr[b])
+        qo_len = int(q_indptr[b + 1]) - q0
+        L = kv_chunk_len(b, page_indptr, last_page_len, 0)
+        j = np.arange(L)
+        page = page_values[int(page_indptr[b]) + j // PAGE_SIZE] if L else np.zeros(0, np.int64)
+        pg_t = torch.from_numpy(np.asarray(page, dtype=np.int64))
+        sl_t = torch.from_numpy(np.asarray(j % PAGE_SIZE, dtype=np.int64))
+        kv = _f64(pages[pg_t, sl_t, :]) if L else np.zeros((0, d_qk))       # [L, d_qk]
+        vis = causal_visible(qi, L, qo_len, causal)
+        tok = q0 + qi
+        qb = _f64(q[tok])                                                    # [n, h_q, d_qk]
+        qr = qb.reshape(len(qi) * h_q, d_qk)
+        o, l = attend(qr, kv, kv[:, :d_latent], np.repeat(vis, h_q, axis=0), sm_scale)
+        out[tok] = o.reshape(len(qi), h_q, d_latent)
+        lse[tok] = l.reshape(len(qi), h_q)
     return out, lse

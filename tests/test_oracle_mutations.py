@@ -35,6 +35,9 @@ PINS = [
     P.test_empty_rows_and_sequences,
     P.test_rope_relative_position_invariance,
     P.test_inkernel_k_rope_equals_cache_rope_at_offset,
+    lambda: P.test_mla_matches_sdpa_on_expanded_heads(1),
+    P.test_mla_absorbed_equals_mha_with_up_projections,
+    P.test_mla_single_visible_key_gives_latent_row,
 ]
 
 _orig_attend = OA.attend
@@ -133,6 +136,21 @@ def _seq_offset_plus_sink(j, b, length_info, sliding_window):
     return np.where(j < sink, j, j + off)          # forgot to subtract the sink
 
 
+def _attend_latent_v_from_last_columns(qr, kr, vr, vis, sm_scale):
+    # latent attention (V narrower than K): V taken from the last columns
+    if vr.shape[1] < kr.shape[1]:
+        vr = kr[:, kr.shape[1] - vr.shape[1]:]
+    return _orig_attend(qr, kr, vr, vis, sm_scale)
+
+
+def _attend_latent_k_without_rope_columns(qr, kr, vr, vis, sm_scale):
+    # latent attention: scores over the latent columns only
+    if vr.shape[1] < kr.shape[1]:
+        n = vr.shape[1]
+        return _orig_attend(qr[:, :n], kr[:, :n], vr, vis, sm_scale)
+    return _orig_attend(qr, kr, vr, vis, sm_scale)
+
+
 def _kv_chunk_len_no_sink(b, page_indptr, length_info, sliding_window):
     n = _orig_kv_chunk_len(b, page_indptr, length_info, sliding_window)
     if sliding_window and n:
@@ -154,6 +172,8 @@ MUTATIONS = {
     "rope_skipped": [("rope", _rope_rounded_identity)],
     "sliding_offset": [("seq_offset", _seq_offset_plus_sink)],
     "chunk_len_no_sink": [("kv_chunk_len", _kv_chunk_len_no_sink)],
+    "latent_v_from_last_columns": [("attend", _attend_latent_v_from_last_columns)],
+    "latent_scores_without_rope_columns": [("attend", _attend_latent_k_without_rope_columns)],
 }
 
 

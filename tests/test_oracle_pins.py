@@ -506,3 +506,109 @@ def test_plain_ragged_prefill_matches_paged_causal():
     ro, rl = oracle.ragged_prefill(w.q, w.q_indptr, k, v, w.kv_store_indptr, None, 0, 1, w.sm_scale)
     np.testing.assert_allclose(ro, po, atol=1e-12)
     np.testing.assert_allclose(rl, pl, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# multi-head latent attention over a latent page pool
+# ---------------------------------------------------------------------------
+
+def _mla(seed, qo, stored, h_q=4, d_qk=24, d_latent=16, causal=1, **kw):
+    from workloads import make_custom_mla
+    return make_custom_mla(seed, qo, stored, h_q=h_q, d_qk=d_qk, d_latent=d_latent, dtype="bf16",
+                           causal=causal, **kw)
+
+
+def _mla_oracle(w, pages=None, **kw):
+    from workloads import mla_pages_from_logical
+    pages = mla_pages_from_logical(w) if pages is None else pages
+    return oracle.mla_paged_attn(w.q, w.q_indptr, pages, w.page_indptr, w.page_values, w.length_info,
+                                 w.causal, w.sm_scale, w.d_latent, **kw)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_mla_matches_sdpa_on_expanded_heads(causal):
+    """Every query head reads the same latent rows: K = all d_qk columns,
+    V = the first d_latent. Against torch SDPA on K/V replicated per head,
+    with an explicit bottom-right mask; lse against scipy's logsumexp."""
+    w = _mla(70, [5, 17, 0, 9, 4], [20, 17, 3, 40, 2], causal=causal)   # last: more queries than keys
+    out, lse = _mla_oracle(w)
+    for b in range(w.batch):
+        q0, q1 = int(w.q_indptr[b]), int(w.q_indptr[b + 1])
+        s0, s1 = int(w.kv_store_indptr[b]), int(w.kv_store_indptr[b + 1])
+        if q1 == q0:
+            continue
+        kv = w.k_store[s0:s1].double().numpy()
+        L, qo = s1 - s0, q1 - q0
+        r = np.arange(qo)[:, None]
+        c = np.arange(L)[None, :]
+        mask = (c < L - qo + r + 1) if causal else np.ones((qo, L), bool)
+        q = w.q[q0:q1].double().numpy()
+        has = mask.any(axis=1)
+        kh = np.repeat(kv[:, None, :], w.h_q, axis=1)
+        vh = np.repeat(kv[:, None, :w.d_latent], w.h_q, axis=1)
+        ref = _sdpa(q[has], kh, vh, mask[has], w.sm_scale)
+        assert np.allclose(out[q0:q1][has], ref, atol=1e-12, rtol=1e-12)
+        assert np.all(out[q0:q1][~has] == 0) and np.all(np.isneginf(lse[q0:q1][~has]))
+        s = w.sm_scale * np.einsum("rhd,ld->rhl", q, kv)
+        s = np.where(mask[:, None, :], s, -np.inf)
+        ref_lse = scipy.special.logsumexp(s[has], axis=-1) / math.log(2.0)
+        assert np.allclose(lse[q0:q1][has], ref_lse, atol=1e-12, rtol=1e-12)
+
+
+def test_mla_absorbed_equals_mha_with_up_projections():
+    """Absorbing the per-head key up-projection into q and the value
+    up-projection after the output gives ordinary attention over the
+    up-projected heads: with K_h = [C W_K,h | K_rope], V_h = C W_V,h and
+    q_h = [q_n,h | q_r,h], MLA over the latent rows [C | K_rope] with
+    q'_h = [q_n,h W_K,h^T | q_r,h] returns out'_h, and out'_h W_V,h equals
+    softmax(q_h K_h^T) V_h (float64, SDPA on the expanded heads)."""
+    rng = np.random.default_rng(71)
+    L, qo, h, dc, dr, dh, dv = 37, 11, 3, 16, 8, 12, 10
+    C = rng.standard_normal((L, dc))
+    K_rope = rng.standard_normal((L, dr))
+    W_K = rng.standard_normal((h, dc, dh)) / 4
+    W_V = rng.standard_normal((h, dc, dv)) / 4
+    q_n = rng.standard_normal((qo, h, dh))
+    q_r = rng.standard_normal((qo, h, dr))
+    scale = 0.3
+    mask = np.arange(L)[None, :] < (L - qo + np.arange(qo)[:, None] + 1)
+    K = np.stack([np.concatenate([C @ W_K[i], K_rope], axis=1) for i in range(h)], axis=1)   # [L, h, dh+dr]
+    V = np.stack([C @ W_V[i] for i in range(h)], axis=1)                                     # [L, h, dv]
+    Q = np.concatenate([q_n, q_r], axis=2)
+    ref = _sdpa(Q, K, V, mask, scale)
+    # latent side: one page table over ceil(L / 16) pages in reverse order
+    npg = (L + 15) // 16
+    pages = torch.zeros((npg, 16, dc + dr), dtype=torch.float64)
+    kv = torch.from_numpy(np.concatenate([C, K_rope], axis=1))
+    order = np.arange(npg)[::-1].astype(np.int32)
+    for t in range(L):
+        pages[order[t // 16], t % 16] = kv[t]
+    q_lat = np.concatenate([np.einsum("rhd,hcd->rhc", q_n, W_K), q_r], axis=2)
+    out_lat, _ = oracle.mla_paged_attn(q_lat, np.array([0, qo]), pages, np.array([0, npg]), order,
+                                       np.array([L - 16 * (npg - 1)]), 1, scale, dc)
+    got = np.einsum("rhc,hcv->rhv", out_lat, W_V)
+    assert np.allclose(got, ref, atol=1e-10, rtol=1e-10)
+
+
+def test_mla_single_visible_key_gives_latent_row():
+    """Causal with no cached prefix: the first query token sees only key 0,
+    so out = its first d_latent values and lse = s_0 / ln 2."""
+    w = _mla(72, [6], [6])
+    out, lse = _mla_oracle(w)
+    kv0 = w.k_store[0].double().numpy()
+    assert np.array_equal(out[0], np.broadcast_to(kv0[:w.d_latent], (w.h_q, w.d_latent)))
+    s0 = w.sm_scale * w.q[0].double().numpy() @ kv0
+    assert np.allclose(lse[0], s0 / math.log(2.0), atol=1e-12)
+
+
+def test_mla_page_permutation_invariance():
+    w = _mla(73, [9, 30], [40, 30], extra_pages=4)
+    out1, lse1 = _mla_oracle(w)
+    from workloads import mla_pages_from_logical
+    pages = mla_pages_from_logical(w)
+    perm = np.random.default_rng(5).permutation(w.num_pages)
+    new_pages = torch.empty_like(pages)
+    new_pages[torch.from_numpy(perm)] = pages
+    w.page_values = perm[w.page_values].astype(np.int32)
+    out2, lse2 = _mla_oracle(w, pages=new_pages)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)

@@ -157,6 +157,10 @@ class Workload:
     # ragged prefill over contiguous K/V (kind "ragged"): padded-batch masks
     pad_mode: int = 0
     valid_len: Optional[np.ndarray] = None          # [b]
+    # multi-head latent attention (kind "mla"): one latent row of d (= d_qk)
+    # values per stored token in k_store, shared by every query head; V is
+    # its first d_latent values. Pages [num_pages, 16, d].
+    d_latent: int = 0
 
     @property
     def total_q(self) -> int:
@@ -168,6 +172,20 @@ class Workload:
 
     def qo_lens(self) -> np.ndarray:
         return np.diff(self.q_indptr)
+
+
+def mla_pages_from_logical(w: Workload) -> torch.Tensor:
+    """Latent page pool [num_pages, 16, d_qk]: stored token t of sequence b in
+    page page_values[page_indptr[b] + t // 16], slot t % 16; other slots zero."""
+    pool = torch.zeros((w.num_pages, PAGE_SIZE, w.d), dtype=TORCH_DTYPES[w.dtype])
+    for b in range(w.batch):
+        s0, s1 = int(w.kv_store_indptr[b]), int(w.kv_store_indptr[b + 1])
+        if s1 == s0:
+            continue
+        t = np.arange(s1 - s0)
+        pg = torch.from_numpy(w.page_values[w.page_indptr[b] + t // PAGE_SIZE].astype(np.int64))
+        pool[pg, torch.from_numpy(t % PAGE_SIZE)] = w.k_store[s0:s1]
+    return pool
 
 
 def pages_from_logical(w: Workload) -> torch.Tensor:
@@ -350,9 +368,37 @@ def make_custom_ragged(seed: int, qo_lens, kv_lens, h_q: int, h_kv: int, d: int,
                     valid_len=None if valid_lens is None else np.asarray(valid_lens, np.int32))
 
 
+def make_custom_mla(seed: int, qo_lens, stored_lens, h_q: int, d_qk: int, d_latent: int, dtype: str,
+                    causal: int = 1, permute_pages: bool = True, extra_pages: int = 0,
+                    sm_scale: Optional[float] = None, name: str = "custom_mla",
+                    rng: Optional[np.random.Generator] = None) -> Workload:
+    """Latent-cache workload: qo_lens[b] query tokens (h_q heads of d_qk)
+    attend to sequence b's stored_lens[b] latent rows (d_qk values each) in
+    pages of 16; the queries are the last qo_lens[b] stored tokens."""
+    rng = _rng(seed) if rng is None else rng
+    b = len(qo_lens)
+    qo_lens = [int(x) for x in qo_lens]
+    stored_lens = [int(x) for x in stored_lens]
+    npages = [(s + PAGE_SIZE - 1) // PAGE_SIZE for s in stored_lens]
+    num_pages = int(sum(npages)) + int(extra_pages)
+    perm = rng.permutation(num_pages).astype(np.int32) if permute_pages else np.arange(num_pages, dtype=np.int32)
+    page_indptr = _indptr(npages)
+    page_values = perm[: int(page_indptr[-1])].copy()
+    last = np.array([s - PAGE_SIZE * (n - 1) if n > 0 else 0 for s, n in zip(stored_lens, npages)], np.int32)
+    q_indptr = _indptr(qo_lens)
+    kv_store_indptr = _indptr(stored_lens)
+    q = _normal(rng, (int(q_indptr[-1]), h_q, d_qk), dtype)
+    kv = _normal(rng, (int(kv_store_indptr[-1]), d_qk), dtype)
+    return Workload(name=name, kind="mla", dtype=dtype, batch=b, h_q=h_q, h_kv=1, d=d_qk,
+                    sm_scale=(1.0 / math.sqrt(d_qk)) if sm_scale is None else sm_scale,
+                    q=q, q_indptr=q_indptr, causal=int(causal), page_indptr=page_indptr,
+                    page_values=page_values, length_info=last, num_pages=num_pages,
+                    kv_store_indptr=kv_store_indptr, k_store=kv, d_latent=int(d_latent))
+
+
 # Workloads beyond the five configurations, for entry points adjacent to
-# the main path (split-KV decode, padded batches).
-EXTRA_NAMES = ("paged_decode", "ragged_left_padded")
+# the main path (split-KV decode, padded batches, latent attention).
+EXTRA_NAMES = ("paged_decode", "ragged_left_padded", "mla_prefill")
 
 
 def make_extra(name: str, seed: Optional[int] = None) -> Workload:
@@ -367,6 +413,18 @@ def make_extra(name: str, seed: Optional[int] = None) -> Workload:
         valid = rng.integers(512, 2049, size=8)
         return make_custom_ragged(seed, [2048] * 8, [2048] * 8, h_q=32, h_kv=8, d=128, dtype="bf16",
                                   causal=1, pad_mode=2, valid_lens=valid, name=name, rng=rng)
+    if name == "mla_prefill":
+        # 8 sequences, qo ~ U[512, 2048] new tokens after a cached prefix
+        # ~ U[0, 2048], 16 query heads (a 128-head model's share at 8-way
+        # head sharding) over a latent cache of 512 + 64 values per token,
+        # bf16, causal; sm_scale 1/sqrt(192) as for 128 + 64-dim heads
+        # before absorption. Seed 2002.
+        seed = 2002 if seed is None else seed
+        rng = _rng(seed)
+        qo = rng.integers(512, 2049, size=8)
+        prefix = rng.integers(0, 2049, size=8)
+        return make_custom_mla(seed, qo, prefix + qo, h_q=16, d_qk=576, d_latent=512, dtype="bf16",
+                               causal=1, sm_scale=1.0 / math.sqrt(192.0), name=name, rng=rng)
     if name != "paged_decode":
         raise KeyError(name)
     seed = 2000 if seed is None else seed

@@ -28,6 +28,7 @@ __all__ = [
     "ra_ragged_prefill",
     "ra_paged_attn_split",
     "ra_paged_attn_split_workspace",
+    "ra_paged_attn_split_noalloc",
     "ra_merge_states",
     "ra_paged_kv_append",
     "ra_set_workgroup_waves",
@@ -39,7 +40,8 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libragattn.so"
 
 EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
-                    "ra_paged_attn_split_workspace", "ra_merge_states", "ra_paged_kv_append",
+                    "ra_paged_attn_split_workspace", "ra_paged_attn_split_noalloc",
+                    "ra_merge_states", "ra_paged_kv_append",
                     "ra_set_workgroup_waves", "ra_attn_workgroup_waves", "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
@@ -82,6 +84,9 @@ def library() -> ctypes.CDLL:
     lib.ra_paged_attn_split.restype = i32
     lib.ra_paged_attn_split.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2 + [i32] * 9
                                         + [i32, i32, f32, f32, f32, i32, vp, ctypes.c_size_t, vp])
+    lib.ra_paged_attn_split_noalloc.restype = i32
+    lib.ra_paged_attn_split_noalloc.argtypes = ([vp] * 6 + [i32] + [vp] * 4 + [i32] + [vp] * 2
+                                                + [i32] * 9 + [i32, i32, f32, f32, f32, i32, vp])
     lib.ra_paged_attn_split_workspace.restype = ctypes.c_size_t
     lib.ra_paged_attn_split_workspace.argtypes = [i32] * 4
     lib.ra_merge_states.restype = i32
@@ -393,6 +398,53 @@ def ra_paged_attn_split(q, q_indptr, pages, page_indptr, page_values, length_inf
         h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
         int(num_kv_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the library's per-GPU partial-state array
+
+
+def ra_paged_attn_split_noalloc(q, q_indptr, pages, page_indptr, page_values, length_info,
+                                sliding_window: int = 0, k_rope_pos_offset=None,
+                                q_rope_position=None, tree_order_indptr=None, tree_order=None,
+                                causal: int = 1, out=None, lse=None, rotary_mode: int = 0,
+                                rope_scale: float = 1.0, rope_theta: float = 1e4,
+                                sm_scale: Optional[float] = None, num_kv_splits: int = 0,
+                                stream=None):
+    """Split-KV paged attention whose partial states live in the library's
+    own per-GPU scratch array (C: ra_paged_attn_split_noalloc): the C call
+    allocates nothing. out and lse must be passed in for a call that
+    allocates nothing here either. Calls overlapping on one GPU race.
+    Returns (out, lse)."""
+    _check_paged_shapes(q, q_indptr, pages, page_indptr, length_info, sliding_window,
+                        k_rope_pos_offset, q_rope_position, tree_order_indptr, tree_order)
+    if rotary_mode == 1:
+        _need(q_rope_position is not None, "rotary_mode 1 needs q_rope_position")
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    _check_dev("pages", pages, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("page_indptr", page_indptr),
+                    ("page_values", page_values), ("length_info", length_info),
+                    ("k_rope_pos_offset", k_rope_pos_offset), ("q_rope_position", q_rope_position),
+                    ("tree_order_indptr", tree_order_indptr), ("tree_order", tree_order)):
+        _check_dev(name, t, i32, dev)
+    out, lse = _out_lse(q, out, lse)
+    total_q, h_q, d = q.shape
+    num_pages, _, h_kv, page_size, _ = pages.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    tree_size = 0 if tree_order is None else tree_order.shape[0]
+    st = library().ra_paged_attn_split_noalloc(
+        _ptr(q), _ptr(q_indptr), _ptr(pages), _ptr(page_indptr), _ptr(page_values),
+        _ptr(length_info), int(sliding_window), _ptr(k_rope_pos_offset), _ptr(q_rope_position),
+        _ptr(tree_order_indptr), _ptr(tree_order), int(causal), _ptr(out), _ptr(lse),
+        q_indptr.numel() - 1, total_q, num_pages, page_values.numel(), tree_size, page_size,
+        h_q, h_kv, d, _DTYPES[q.dtype], rotary_mode, rope_scale, rope_theta, sm_scale,
+        int(num_kv_splits), _stream(dev, stream))
     _raise(st)
     return out, lse
 

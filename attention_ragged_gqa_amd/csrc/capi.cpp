@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "ra_internal.h"
 #include "../../include/ragattn.h"
@@ -354,6 +355,87 @@ ra_status ra_paged_attn_split(const void* q, const int32_t* q_indptr, const void
                          tree_size, page_size, h_q, h_kv, head_dim, dtype, rotary_mode,
                          rope_scale, rope_theta, sm_scale, num_kv_splits, workspace,
                          workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- split-KV without a caller workspace ---------------------------------
+// The partial states live in a file-scope device array, one copy per GPU,
+// held until the process ends. `scratch` names the host-side shadow of that
+// array: host code never passes it to a kernel, it passes the device address
+// hipGetSymbolAddress returns for the GPU the launch runs on (kept per
+// device below). Nothing in it has to start at zero: every (split, row)
+// partial the merge reads is written by the attention kernel of the same
+// call first.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of this GPU's scratch array, looked up once per device with
+// that device current. dev: the device the caller's stream belongs to.
+ra_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(RA_EHIP, "hipGetDevice failed");
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    const hipError_t e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return fail(RA_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    dev = static_cast<int>(d);
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(RA_EUNSUPPORTED, "device %d beyond %d", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return fail(RA_EHIP, "hipSetDevice(%d) failed", dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(RA_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_paged_attn_split_noalloc(const void* q, const int32_t* q_indptr, const void* pages,
+                                      const int32_t* page_indptr, const int32_t* page_values,
+                                      const int32_t* length_info, int32_t sliding_window,
+                                      const int32_t* k_rope_pos_offset,
+                                      const int32_t* q_rope_position,
+                                      const int32_t* tree_order_indptr, const int32_t* tree_order,
+                                      int32_t causal, void* out, float* lse, int32_t batch,
+                                      int32_t total_q, int32_t num_pages, int32_t nnz_pages,
+                                      int32_t tree_size, int32_t page_size, int32_t h_q,
+                                      int32_t h_kv, int32_t head_dim, ra_dtype dtype,
+                                      int32_t rotary_mode, float rope_scale, float rope_theta,
+                                      float sm_scale, int32_t num_kv_splits, hipStream_t stream) {
+  // explicit split counts whose partial states exceed the array are refused
+  // before anything else (the automatic count is chosen to fit)
+  if (num_kv_splits > 1 && num_kv_splits <= kMaxSplits &&
+      split_workspace_bytes(total_q, h_q, head_dim, num_kv_splits) > kScratchBytes)
+    return fail(RA_EINVAL, "%d splits need %zu bytes of partial states, beyond the %zu-byte scratch array",
+                num_kv_splits, split_workspace_bytes(total_q, h_q, head_dim, num_kv_splits), kScratchBytes);
+  void* ws = nullptr;
+  if (num_kv_splits != 1 && total_q > 0 && batch > 0) {
+    const ra_status st = scratch_address(stream, &ws);
+    if (st != RA_OK) return st;
+  }
+  return paged_attn_impl(q, q_indptr, pages, page_indptr, page_values, length_info,
+                         sliding_window, k_rope_pos_offset, q_rope_position, tree_order_indptr,
+                         tree_order, causal, out, lse, batch, total_q, num_pages, nnz_pages,
+                         tree_size, page_size, h_q, h_kv, head_dim, dtype, rotary_mode,
+                         rope_scale, rope_theta, sm_scale, num_kv_splits, ws,
+                         ws != nullptr ? kScratchBytes : 0, stream);
 }
 
 ra_status ra_merge_states(const float* part_out, const float* part_lse, int32_t num_splits,

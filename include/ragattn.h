@@ -4,7 +4,8 @@
  * C ABI of libragattn.so. Every entry point launches asynchronously on the
  * caller's HIP stream, never synchronises, allocates no device memory and
  * keeps no state between calls (apart from the process-wide workgroup shape
- * that ra_set_workgroup_waves may fix). Pointers are caller-owned device memory
+ * that ra_set_workgroup_waves may fix, and the per-GPU scratch array of
+ * ra_paged_attn_split_noalloc). Pointers are caller-owned device memory
  * unless stated otherwise; inputs are read-only. Index arrays are int32.
  *
  * Operation defined by the TVM pages (cited by page and section):
@@ -185,6 +186,35 @@ ra_status ra_paged_attn_split(const void* q, const int32_t* q_indptr, const void
                               float rope_scale, float rope_theta, float sm_scale,
                               int32_t num_kv_splits, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * ra_paged_attn_split without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and result as
+ * ra_paged_attn_split minus the workspace: the partial states go to a
+ * 32 MiB (33554432-byte) array of device memory that the library holds, one
+ * copy per GPU, from the first call on that GPU until the process ends. The
+ * call allocates nothing. num_kv_splits 0 picks the split count as
+ * ra_paged_attn_split does, limited to what fits the array (falling back to
+ * the unsplit kernel); an explicit count whose partial states need more
+ * than 32 MiB (see ra_paged_attn_split_workspace) returns RA_EINVAL. Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and give wrong results;
+ * calls ordered on one stream are safe. Errors as ra_paged_attn_split, and
+ * RA_EHIP when the array's device address cannot be obtained.
+ */
+ra_status ra_paged_attn_split_noalloc(const void* q, const int32_t* q_indptr, const void* pages,
+                                      const int32_t* page_indptr, const int32_t* page_values,
+                                      const int32_t* length_info, int32_t sliding_window,
+                                      const int32_t* k_rope_pos_offset,
+                                      const int32_t* q_rope_position,
+                                      const int32_t* tree_order_indptr, const int32_t* tree_order,
+                                      int32_t causal, void* out, float* lse, int32_t batch,
+                                      int32_t total_q, int32_t num_pages, int32_t nnz_pages,
+                                      int32_t tree_size, int32_t page_size, int32_t h_q,
+                                      int32_t h_kv, int32_t head_dim, ra_dtype dtype,
+                                      int32_t rotary_mode, float rope_scale, float rope_theta,
+                                      float sm_scale, int32_t num_kv_splits, hipStream_t stream);
 
 /* Bytes of workspace ra_paged_attn_split needs for num_kv_splits ranges
  * (0 when num_kv_splits <= 1): num_kv_splits * total_q * h_q * (head_dim + 1)

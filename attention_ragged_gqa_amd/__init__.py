@@ -30,6 +30,7 @@ __all__ = [
     "ra_paged_attn_split_workspace",
     "ra_paged_attn_split_noalloc",
     "ra_merge_states",
+    "ra_mla_paged_prefill",
     "ra_paged_kv_append",
     "ra_set_workgroup_waves",
     "ra_attn_workgroup_waves",
@@ -41,7 +42,7 @@ LIB_NAME = "libragattn.so"
 
 EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
                     "ra_paged_attn_split_workspace", "ra_paged_attn_split_noalloc",
-                    "ra_merge_states", "ra_paged_kv_append",
+                    "ra_merge_states", "ra_mla_paged_prefill", "ra_paged_kv_append",
                     "ra_set_workgroup_waves", "ra_attn_workgroup_waves", "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
@@ -91,6 +92,8 @@ def library() -> ctypes.CDLL:
     lib.ra_paged_attn_split_workspace.argtypes = [i32] * 4
     lib.ra_merge_states.restype = i32
     lib.ra_merge_states.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.ra_mla_paged_prefill.restype = i32
+    lib.ra_mla_paged_prefill.argtypes = [vp] * 6 + [i32, vp, vp] + [i32] * 8 + [i32, f32, vp]
     lib.ra_paged_kv_append.restype = i32
     lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
     lib.ra_set_workgroup_waves.restype = i32
@@ -466,6 +469,54 @@ def ra_merge_states(part_out, part_lse, out, lse, stream=None):
         raise ValueError("shapes: part_out [S, rows, d], part_lse [S, rows], out rows*d, lse rows")
     st = library().ra_merge_states(_ptr(part_out), _ptr(part_lse), S, rows, d, _DTYPES[out.dtype],
                                    _ptr(out), _ptr(lse), _stream(dev, stream))
+    _raise(st)
+    return out, lse
+
+
+def ra_mla_paged_prefill(q, q_indptr, pages, page_indptr, page_values, last_page_len,
+                         causal: int = 1, d_latent: int = 512, out=None, lse=None,
+                         sm_scale: Optional[float] = None, stream=None):
+    """Multi-head latent attention over a paged latent cache
+    (C: ra_mla_paged_prefill). q [total_q, h_q, d_qk]; pages
+    [num_pages, 16, d_qk], one latent row per cached token shared by every
+    head (K = all d_qk values, V = the first d_latent); last_page_len [b].
+    Returns (out [total_q, h_q, d_latent], lse [total_q, h_q])."""
+    _need(q.dim() == 3, "q must be [total_q, h_q, d_qk] (got %d dims)", q.dim())
+    _need(q_indptr is not None and q_indptr.dim() == 1 and q_indptr.numel() >= 1,
+          "q_indptr must be a [batch + 1] array")
+    batch = q_indptr.numel() - 1
+    _need(pages.dim() == 3 and pages.shape[2] == q.shape[2],
+          "pages must be [num_pages, page_size, d_qk] with q's d_qk (got %s)", tuple(pages.shape))
+    _need(0 < d_latent <= q.shape[2], "d_latent must be in (0, d_qk]")
+    _check_indptr("page_indptr", page_indptr, batch)
+    _numel_is("last_page_len", last_page_len, batch)
+    _need(last_page_len is not None, "last_page_len is required")
+    dev = q.device
+    i32 = torch.int32
+    _check_dev("q", q, None, dev)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be fp16 or bf16")
+    _check_dev("pages", pages, q.dtype, dev)
+    for name, t in (("q_indptr", q_indptr), ("page_indptr", page_indptr),
+                    ("page_values", page_values), ("last_page_len", last_page_len)):
+        _check_dev(name, t, i32, dev)
+    total_q, h_q, d_qk = q.shape
+    if out is None:
+        out = torch.empty(total_q, h_q, d_latent, dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(total_q, h_q, dtype=torch.float32, device=dev)
+    _check_dev("out", out, q.dtype, dev)
+    _check_dev("lse", lse, torch.float32, dev)
+    _need(tuple(out.shape) == (total_q, h_q, d_latent) and tuple(lse.shape) == (total_q, h_q),
+          "out must be [total_q, h_q, d_latent] and lse [total_q, h_q]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_qk)
+    num_pages, page_size, _ = pages.shape
+    st = library().ra_mla_paged_prefill(
+        _ptr(q), _ptr(q_indptr), _ptr(pages), _ptr(page_indptr), _ptr(page_values),
+        _ptr(last_page_len), int(causal), _ptr(out), _ptr(lse), batch, total_q, num_pages,
+        page_values.numel(), page_size, h_q, d_qk, d_latent, _DTYPES[q.dtype], sm_scale,
+        _stream(dev, stream))
     _raise(st)
     return out, lse
 

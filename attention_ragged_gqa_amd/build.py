@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libragattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["attn_fwd.hip", "kv_append.hip", "merge.hip", "capi.cpp"]
+SOURCES = ["attn_fwd.hip", "mla_fwd.hip", "kv_append.hip", "merge.hip", "capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -438,6 +438,49 @@ ra_status ra_paged_attn_split_noalloc(const void* q, const int32_t* q_indptr, co
                          ws != nullptr ? kScratchBytes : 0, stream);
 }
 
+ra_status ra_mla_paged_prefill(const void* q, const int32_t* q_indptr, const void* pages,
+                               const int32_t* page_indptr, const int32_t* page_values,
+                               const int32_t* last_page_len, int32_t causal, void* out, float* lse,
+                               int32_t batch, int32_t total_q, int32_t num_pages,
+                               int32_t nnz_pages, int32_t page_size, int32_t h_q, int32_t d_qk,
+                               int32_t d_latent, ra_dtype dtype, float sm_scale,
+                               hipStream_t stream) {
+  if (batch < 0 || total_q < 0 || num_pages < 0 || nnz_pages < 0)
+    return fail(RA_EINVAL, "negative batch, total_q, num_pages or nnz_pages");
+  if (h_q <= 0) return fail(RA_EINVAL, "h_q must be positive, got %d", h_q);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(RA_EINVAL, "sm_scale must be finite and > 0");
+  if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported (fp16=0, bf16=1)", (int)dtype);
+  if (d_latent != 512 || d_qk != 576)
+    return fail(RA_EUNSUPPORTED, "latent widths (d_qk %d, d_latent %d) not supported (576, 512)", d_qk, d_latent);
+  if (page_size != 16) return fail(RA_EUNSUPPORTED, "page_size %d not supported (16)", page_size);
+  ra_status st = check_limits(total_q, h_q, 0, nnz_pages);
+  if (st != RA_OK) return st;
+  if (batch > 0 && (q_indptr == nullptr || page_indptr == nullptr || last_page_len == nullptr))
+    return fail(RA_EINVAL, "q_indptr, page_indptr and last_page_len must be non-NULL");
+  if (total_q > 0 && (q == nullptr || out == nullptr || lse == nullptr))
+    return fail(RA_EINVAL, "q, out and lse must be non-NULL");
+  if (nnz_pages > 0 && page_values == nullptr) return fail(RA_EINVAL, "page_values is NULL");
+  if (num_pages > 0 && pages == nullptr) return fail(RA_EINVAL, "pages is NULL");
+  if (batch == 0 || total_q == 0) return ok();
+  ra::MlaParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_indptr = q_indptr;
+  p.pages = static_cast<const uint16_t*>(pages);
+  p.page_indptr = page_indptr;
+  p.page_values = page_values;
+  p.last_page_len = last_page_len;
+  p.out = out;
+  p.lse = lse;
+  p.batch = batch;
+  p.total_q = total_q;
+  p.h_q = h_q;
+  p.num_pages = num_pages;
+  p.nnz_pages = nnz_pages;
+  p.causal = causal != 0;
+  p.sm_scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  return launched(ra::launch_mla(p, dtype == RA_BF16, stream));
+}
+
 ra_status ra_merge_states(const float* part_out, const float* part_lse, int32_t num_splits,
                           int32_t rows, int32_t head_dim, ra_dtype dtype, void* out, float* lse,
                           hipStream_t stream) {

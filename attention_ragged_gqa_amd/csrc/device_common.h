@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 namespace ra {
@@ -81,6 +82,56 @@ __device__ __forceinline__ f32x16 mma32(const u32x4& a, const u32x4& b, const f3
   }
 }
 
+// ---- memory helpers ----------------------------------------------------------
+// Bounds-checked loads through a buffer resource: offsets at or past the end
+// of the range (negative offsets wrap past it) read as zero, with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = static_cast<int>(min(max(bytes, 0L), static_cast<long>(INT_MAX)));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+__device__ __forceinline__ int load_i32(__amdgpu_buffer_rsrc_t r, int index) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, 0);
+}
+__device__ __forceinline__ int2 load_i32x2(__amdgpu_buffer_rsrc_t r, int index) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, index * 8, 0, 0);
+  return make_int2(static_cast<int>(v[0]), static_cast<int>(v[1]));
+}
+// An opaque use of a loaded value at the point where it is needed: without it
+// the compiler moves dependent arithmetic up to the load and waits there,
+// before the remaining loads of the prologue have been issued.
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(double& x) { asm volatile("" : "+v"(x)); }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base wave-uniform, passed in M0). Issued through
+// inline asm so the compiler does not treat these asynchronous LDS writes as
+// aliasing every later LDS read (it would wait for them before each read and
+// undo the prefetch); wait_all_and_barrier() orders them explicitly.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const unsigned lds = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+}
+
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (the saddr form: no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void dma16s(const char* sbase, uint32_t voff, const void* lds_base) {
+  const unsigned lds = static_cast<unsigned>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) const char*)lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// Wait for this wave's outstanding global loads (including loads into LDS)
+// and LDS accesses, then the workgroup barrier. Written out because the
+// compiler neither tracks loads into LDS nor should it fence in between.
+__device__ __forceinline__ void wait_all_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Free (everything has retired), but visible to the compiler: loads it
+  // tracks need no further waits before the next DMA is issued.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+}
+
 // ---- wave reductions (wave64) ---------------------------------------------
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -96,6 +147,69 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
     if (lane >= d) x += y;
   }
   return x;
+}
+
+// Locate this workgroup's work item. Returns false when the block has none.
+// Item list: for each KV head, for each sequence b (in order), ranks
+// 0..tiles_b-1 with rank 0 = the last (heaviest under a causal mask) q-tile.
+// KV-head-major order: with the list cut into 8 equal chunks (one per XCD),
+// every XCD gets the same mix of long and short sequences (exactly one KV
+// head each when h_kv = 8), while all tiles of one (sequence, KV head) still
+// share an XCD's L2.
+// With split-KV (splits > 1) each q-tile is `splits` items, one per KV range.
+// Also returns the sequence's query offset q0 and length qo_len.
+__device__ inline bool locate_item(const int32_t* q_indptr, int batch, int group, int h_kv, int splits, int bm,
+                            int& b, int& kvh, int& tile, int& split, int& q0, int& qo_len) {
+  const int lane = threadIdx.x & 63;
+  // q-tiles of sequence i, and its query range
+  auto count = [&](int i, int& lo, int& len) __attribute__((always_inline)) -> int {
+    lo = 0;
+    len = 0;
+    if (i >= batch) return 0;
+    lo = q_indptr[i];
+    len = max(q_indptr[i + 1] - lo, 0);
+    return (len * group + bm - 1) / bm * splits;
+  };
+  int lo0, len0;
+  const int cnt0 = count(lane, lo0, len0);   // first 64 sequences, kept for the search
+  int per_head = wave_sum(cnt0);
+  for (int c0 = 64; c0 < batch; c0 += 64) {
+    int lo, len;
+    per_head += wave_sum(count(c0 + lane, lo, len));
+  }
+  const int total = per_head * h_kv;
+  // XCD-contiguous mapping: block L runs on XCD L % 8; give XCD x the items
+  // [x*chunk, (x+1)*chunk) in order.
+  const int chunk = (total + 7) / 8;
+  const int L = blockIdx.x;
+  const int slot = L >> 3;
+  if (slot >= chunk) return false;
+  const int item = (L & 7) * chunk + slot;
+  if (item >= total) return false;
+  kvh = item / per_head;
+  const int rem = item - kvh * per_head;
+  int base = 0;
+  for (int c0 = 0; c0 < batch; c0 += 64) {
+    int lo = lo0, len = len0, cnt = cnt0;
+    if (c0 > 0) cnt = count(c0 + lane, lo, len);
+    const int incl = wave_inclusive_scan(cnt) + base;
+    const unsigned long long hit = __ballot(c0 + lane < batch && rem < incl);
+    if (hit) {
+      const int l = __ffsll(static_cast<long long>(hit)) - 1;
+      b = c0 + l;
+      const int excl = __shfl(incl - cnt, l, 64);
+      const int tiles_b = __shfl(cnt, l, 64) / splits;
+      q0 = __shfl(lo, l, 64);
+      qo_len = __shfl(len, l, 64);
+      const int local = rem - excl;
+      const int rank = local / splits;
+      split = local - rank * splits;
+      tile = tiles_b - 1 - rank;
+      return true;
+    }
+    base = __shfl(incl, 63, 64);
+  }
+  return false;
 }
 
 // ---- lane l and lane l ^ 32 (v_permlane32_swap, no LDS traffic) ----------

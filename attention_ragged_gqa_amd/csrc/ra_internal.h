@@ -80,6 +80,22 @@ struct AppendParams {
   double inv_freq[64];     // RoPE: theta^(-2k/head_dim), k < head_dim / 2
 };
 
+// Multi-head latent attention prefill over a paged latent cache
+// (mla_fwd.hip): one KV row of d_qk = 512 + 64 values per token, read as K
+// over all of them and as V over the first 512.
+struct MlaParams {
+  const uint16_t* q;             // [total_q, h_q, 576]
+  const int32_t* q_indptr;
+  const uint16_t* pages;         // [num_pages, 16, 576]
+  const int32_t* page_indptr;
+  const int32_t* page_values;
+  const int32_t* last_page_len;  // [batch]
+  void* out;                     // [total_q, h_q, 512]
+  float* lse;                    // [total_q, h_q]
+  int32_t batch, total_q, h_q, num_pages, nnz_pages, causal;
+  float sm_scale_log2;           // sm_scale * log2(e)
+};
+
 // Launchers (attn_fwd.hip / kv_append.hip). Return the hipError_t of the launch.
 // Waves per workgroup (4 or 8) that launch_attn uses for p: the work item is
 // 32 packed query rows per wave. set_waves_override(0 | 4 | 8) fixes it for
@@ -90,5 +106,6 @@ hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout 
                        MaskKind mask, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int is_bf16, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int is_bf16, int head_dim, hipStream_t stream);
+hipError_t launch_mla(const MlaParams& p, int is_bf16, hipStream_t stream);
 
 }  // namespace ra

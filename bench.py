@@ -123,6 +123,13 @@ def visible_pairs(w, seqs=None) -> int:
     return total * w.h_q
 
 
+def flops_per_pair(w) -> float:
+    """2 d_qk for the score and 2 d_v for the PV product of one unmasked
+    (row, head, key) pair: 4 d, or 2 (576 + 512) for latent attention."""
+    d_v = w.d_latent if w.kind == "mla" else w.d
+    return 2.0 * (w.d + d_v)
+
+
 def algorithmic_bytes(w) -> int:
     """Q and out (dtype) + every visible K/V row read once (dtype) + lse (fp32)
     + index arrays (indptrs, tree intervals, page table entries, positions)."""
@@ -134,6 +141,11 @@ def algorithmic_bytes(w) -> int:
     if w.kind == "ragged" and w.pad_mode != 0:   # only the valid rows are read
         v = np.asarray(w.valid_len, np.int64)
         kv_rows = int(np.sum(np.where(np.minimum(v, qo) > 0, np.clip(np.minimum(v, L), 0, None), 0)))
+    if w.kind == "mla":   # q + out (latent width) + lse, one shared latent row per key
+        nbytes = total_q * w.h_q * (w.d + w.d_latent) * esz + total_q * w.h_q * 4
+        nbytes += kv_rows * w.d * esz
+        nbytes += 4 * (w.batch + 1) * 2 + 4 * int(np.sum((L + 15) // 16)) + 4 * w.batch
+        return int(nbytes)
     nbytes = 2 * total_q * w.h_q * w.d * esz + total_q * w.h_q * 4
     nbytes += kv_rows * w.h_kv * w.d * 2 * esz
     nbytes += 4 * (w.batch + 1) * 2                       # q_indptr + kv/page indptr
@@ -154,7 +166,8 @@ def config_summary(w) -> dict:
     qo = np.diff(w.q_indptr)
     c = {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
          "total_q": w.total_q, "qo_len_range": [int(qo.min()), int(qo.max())],
-         "kv_layout": "contiguous" if w.kind in ("tree", "ragged") else "paged16",
+         "kv_layout": "contiguous" if w.kind in ("tree", "ragged") else
+                      ("paged16 latent (%d + %d)" % (w.d_latent, w.d - w.d_latent) if w.kind == "mla" else "paged16"),
          "mask": {1: "right-padded", 2: "left-padded causal"}[w.pad_mode]
                  if (w.kind == "ragged" and w.pad_mode) else
                  "tree" if (w.kind == "tree" or w.tree_order is not None) else
@@ -164,7 +177,7 @@ def config_summary(w) -> dict:
          "sm_scale": w.sm_scale}
     if w.kind == "ragged" and w.pad_mode:
         c["valid_len_range"] = [int(np.min(w.valid_len)), int(np.max(w.valid_len))]
-    if w.kind == "paged":
+    if w.kind in ("paged", "mla"):
         c["kv_chunk_range"] = [int(chunk_lengths(w).min()), int(chunk_lengths(w).max())]
         c["num_pages"] = w.num_pages
     return c
@@ -174,9 +187,15 @@ def config_summary(w) -> dict:
 # rocprofv3 counter summary (traffic)
 # ---------------------------------------------------------------------------
 
-def kernel_source_hash() -> str:
+def kernel_name(workload: str) -> str:
+    """The dominant kernel of a workload's step."""
+    return "mla_fwd_kernel" if workload.startswith("mla") else KERNEL_NAME
+
+
+def kernel_source_hash(kernel: str = KERNEL_NAME) -> str:
+    src = "mla_fwd.hip" if kernel == "mla_fwd_kernel" else "attn_fwd.hip"
     h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "device_common.h", "ra_internal.h"):
+    for name in (src, "device_common.h", "ra_internal.h"):
         with open(os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -185,13 +204,14 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (KERNEL_NAME, workload))
+    kernel = kernel_name(workload)
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (kernel, workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(kernel):
         return None
     return int(m_bytes.group(1))
 
@@ -213,7 +233,8 @@ def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
         cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    pool = pages_from_logical(w) if w.kind == "paged" else None
+    from workloads import mla_pages_from_logical
+    pool = pages_from_logical(w) if w.kind == "paged" else (mla_pages_from_logical(w) if w.kind == "mla" else None)
     if w.total_q * w.h_q <= 64 * 1024:
         n, t0 = 0, time.perf_counter()
         while True:
@@ -239,7 +260,7 @@ def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
         sample = ("sequences 0..%d of %d (every query row and head of each, %.2f%% of the "
                   "workload's unmasked pairs), pairs counted exactly" % (done - 1, w.batch,
                                                                         100.0 * pairs / pairs_per_pass))
-    tflops = 4.0 * w.d * pairs / el / 1e12
+    tflops = flops_per_pair(w) * pairs / el / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(el, 3), "estimated": False,
             "cpu": _cpu_model()}
@@ -273,7 +294,7 @@ def copy_calibration(steps: int):
 
 def bound_of(w) -> str:
     """'mfma' when the workload's flop/byte ratio is above the ridge point."""
-    ai = 4.0 * w.d * visible_pairs(w) / algorithmic_bytes(w)
+    ai = flops_per_pair(w) * visible_pairs(w) / algorithmic_bytes(w)
     return "mfma" if ai > PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
 
 
@@ -334,7 +355,7 @@ def time_steps(dis, steps: int, warmup: int, graph_launches: int, launch_kw: dic
 def rates(w, ms_step: float) -> dict:
     """Throughput and roofline fractions of one step of w taking ms_step."""
     pairs = visible_pairs(w)
-    flops = 4.0 * w.d * pairs
+    flops = flops_per_pair(w) * pairs
     nbytes = algorithmic_bytes(w)
     t_s = ms_step / 1e3
     tflops = flops / t_s / 1e12
@@ -441,7 +462,7 @@ def main():
     roof["traffic"] = measured_traffic(w.name)
     roof["algorithmic_bytes"] = r["bytes"]
     roof["algorithmic_flops"] = r["flops"]
-    roof["kernel"] = KERNEL_NAME
+    roof["kernel"] = kernel_name(w.name)
 
     line = {
         "metric": METRIC, "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1,

@@ -238,6 +238,40 @@ ra_status ra_merge_states(const float* part_out, const float* part_lse, int32_t 
                           hipStream_t stream);
 
 /*
+ * Multi-head latent attention prefill over a paged latent cache
+ * ("_kernel_common.py" page: AttnKind MLA; _alloc_mla_qkvo_buffers, whose
+ * single KV tile of d_qk columns serves as K over all of them and as V over
+ * the first d_latent; paged_store_output_lse with every query head in one
+ * group; _causal_mask).
+ *
+ * Every token of a sequence has one cached row of d_qk values shared by all
+ * h_q query heads (a compressed latent vector of d_latent values followed by
+ * its rotary part). For query token i of sequence b and head h:
+ *   s_j = sm_scale * sum_{t < d_qk} q[i,h,t] * kv_j[t]
+ *   out[i,h,:] = sum_j softmax(s)_j * kv_j[0 : d_latent]     (stored in dtype)
+ *   lse[i,h]   = log2(sum_j exp(s_j))                        (float32)
+ * over the keys j < kv_len - qo_len + i + 1 (causal != 0) or j < kv_len.
+ * Layouts (row-major): q [total_q, h_q, d_qk]; out [total_q, h_q, d_latent];
+ * lse [total_q, h_q]; pages [num_pages, page_size, d_qk]. Sequence b owns
+ * pages page_values[page_indptr[b] .. page_indptr[b+1]); with np pages its
+ * chunk holds kv_len = (np-1)*page_size + last_page_len[b] rows (0 when
+ * np == 0), row o in page page_values[page_indptr[b] + o / page_size], slot
+ * o % page_size. Any RoPE on q and on the cached rotary part is applied by
+ * the caller. A row with no visible key gets out = 0 and lse = -inf.
+ * Supported: d_qk = 576 and d_latent = 512 (RA_EUNSUPPORTED otherwise),
+ * page_size 16, fp16/bf16, any h_q. nnz_pages = page_indptr[batch].
+ * Errors: RA_EINVAL (NULL pointers, negative sizes, sm_scale), RA_EUNSUPPORTED,
+ * RA_EHIP (launch).
+ */
+ra_status ra_mla_paged_prefill(const void* q, const int32_t* q_indptr, const void* pages,
+                               const int32_t* page_indptr, const int32_t* page_values,
+                               const int32_t* last_page_len, int32_t causal, void* out, float* lse,
+                               int32_t batch, int32_t total_q, int32_t num_pages,
+                               int32_t nnz_pages, int32_t page_size, int32_t h_q, int32_t d_qk,
+                               int32_t d_latent, ra_dtype dtype, float sm_scale,
+                               hipStream_t stream);
+
+/*
  * Append new K/V tokens into the paged cache, rotating K first when
  * rope_position is non-NULL (the "normal" RoPE mode of the KV cache on the
  * "_kernel_common.py" page, RopeMode: RoPE applied to k before adding it to

@@ -45,6 +45,12 @@ def run_oracle(w, rows=None, pool=None):
     """The oracle on workload w (rows: global query tokens to evaluate, all
     when None). pool: the page pool of a paged workload as
     pages_from_logical(w) returns it, when the caller has built it already."""
+    if w.kind == "mla":
+        from workloads import mla_pages_from_logical
+        if pool is None:
+            pool = mla_pages_from_logical(w)
+        return oracle.mla_paged_attn(w.q, w.q_indptr, pool, w.page_indptr, w.page_values,
+                                     w.length_info, w.causal, w.sm_scale, w.d_latent, rows=rows)
     if w.kind == "ragged":
         return oracle.ragged_prefill(w.q, w.q_indptr, w.k, w.v, w.kv_indptr, w.valid_len,
                                      w.pad_mode, w.causal, w.sm_scale, rows=rows)

@@ -99,3 +99,16 @@ def test_cpu_baseline_counts_what_it_times():
 def test_bound_of_configs():
     assert bench.bound_of(make_config(1)) == "hbm"
     assert bench.bound_of(make_config(2)) == "mfma"
+
+
+def test_latent_attention_accounting():
+    from workloads import make_custom_mla
+    w = make_custom_mla(11, [5, 0, 7], [20, 4, 7], h_q=4, d_qk=576, d_latent=512, dtype="bf16", causal=1)
+    # causal rows: sequence 0 sees 16..20 keys, sequence 2 sees 1..7
+    pairs = (sum(range(16, 21)) + sum(range(1, 8))) * 4
+    assert bench.visible_pairs(w) == pairs
+    assert bench.flops_per_pair(w) == 2 * (576 + 512)
+    q_out = 12 * 4 * (576 + 512) * 2 + 12 * 4 * 4
+    kv = (20 + 7) * 576 * 2                     # one latent row per key of the sequences with queries
+    idx = 4 * 4 * 2 + 4 * (2 + 1 + 1) + 4 * 3
+    assert bench.algorithmic_bytes(w) == q_out + kv + idx

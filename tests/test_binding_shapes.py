@@ -137,3 +137,28 @@ def test_ragged_prefill_rejects_shapes(over):
 ])
 def test_append_rejects_shapes(over):
     _shape_error(ra.ra_paged_kv_append, _append_args(**over))
+
+
+def _mla_args(**over):
+    a = dict(q=torch.zeros(10, 16, 576, dtype=F16), q_indptr=torch.tensor([0, 4, 10], dtype=I32),
+             pages=torch.zeros(5, 16, 576, dtype=F16), page_indptr=torch.tensor([0, 2, 5], dtype=I32),
+             page_values=torch.arange(5, dtype=I32), last_page_len=torch.tensor([3, 16], dtype=I32))
+    a.update(over)
+    return a
+
+
+def test_mla_well_shaped_call_reaches_the_device_check():
+    _passes_shape_checks(ra.ra_mla_paged_prefill, _mla_args())
+
+
+@pytest.mark.parametrize("over", [
+    dict(pages=torch.zeros(5, 16, 512, dtype=F16)),                   # d_qk differs from q
+    dict(pages=torch.zeros(5, 2, 16, 576, dtype=F16)),                # per-head K/V pages
+    dict(page_indptr=torch.tensor([0, 5], dtype=I32)),
+    dict(last_page_len=torch.tensor([3], dtype=I32)),
+    dict(last_page_len=None),
+    dict(d_latent=600),
+    dict(q=torch.zeros(10, 576, dtype=F16)),
+])
+def test_mla_rejects_shapes(over):
+    _shape_error(ra.ra_mla_paged_prefill, _mla_args(**over))

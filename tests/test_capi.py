@@ -226,3 +226,27 @@ def test_workgroup_waves_policy(lib):
     finally:
         ra.ra_set_workgroup_waves(0)
     assert q(32768, 64, 8) == 8
+
+
+def test_mla_rejects(lib):
+    P = ctypes.c_void_p(0x1000)
+
+    def call(batch=1, total_q=4, num_pages=4, nnz=4, page=16, h_q=16, d_qk=576, d_lat=512, dtype=1,
+             sm=0.07, ptrs=None):
+        p = dict(q=P, q_indptr=P, pages=P, page_indptr=P, page_values=P, last=P, out=P, lse=P)
+        p.update(ptrs or {})
+        return lib.ra_mla_paged_prefill(p["q"], p["q_indptr"], p["pages"], p["page_indptr"],
+                                        p["page_values"], p["last"], 1, p["out"], p["lse"], batch,
+                                        total_q, num_pages, nnz, page, h_q, d_qk, d_lat, dtype, sm, None)
+    assert call(d_qk=192, d_lat=128) == ra.RA_EUNSUPPORTED     # only the 512 + 64 latent shape
+    assert call(d_lat=256) == ra.RA_EUNSUPPORTED
+    assert call(page=32) == ra.RA_EUNSUPPORTED
+    assert call(dtype=5) == ra.RA_EUNSUPPORTED
+    assert call(h_q=0) == ra.RA_EINVAL
+    assert call(sm=0.0) == ra.RA_EINVAL
+    assert call(batch=-1) == ra.RA_EINVAL
+    assert call(ptrs={"last": None}) == ra.RA_EINVAL
+    assert call(ptrs={"page_values": None}) == ra.RA_EINVAL
+    assert call(ptrs={"out": None}) == ra.RA_EINVAL
+    assert call(total_q=(1 << 31) // 16, h_q=16) == ra.RA_EUNSUPPORTED
+    assert call(batch=0, total_q=0) == ra.RA_OK

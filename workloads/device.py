@@ -11,7 +11,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .generators import pages_from_logical
+from .generators import mla_pages_from_logical, pages_from_logical
 
 
 def _i32(a, dev):
@@ -68,7 +68,8 @@ class DeviceInputs:
         self.q_indptr = _i32(w.q_indptr, d)
         self.q_rope_position = _i32(w.q_rope_position, d) if w.rotary_mode == 1 else None
         # poisoned: a row the kernels never write stays NaN
-        self.out = torch.full_like(self.q, float("nan"))
+        out_d = w.d_latent if w.kind == "mla" else w.d
+        self.out = torch.full((w.total_q, w.h_q, out_d), float("nan"), dtype=w.q.dtype, device=d)
         self.lse = torch.full((w.total_q, w.h_q), float("nan"), dtype=torch.float32, device=d)
         if w.kind == "tree":
             self.k = w.k.to(d)
@@ -76,6 +77,11 @@ class DeviceInputs:
             self.kv_indptr = _i32(w.kv_indptr, d)
             self.mn_indptr = _i32(w.mn_indptr, d)
             self.tree_mask = _i32(w.tree_mask.reshape(-1, 2), d)
+        elif w.kind == "mla":
+            self.pages = mla_pages_from_logical(w).to(d)
+            self.page_indptr = _i32(w.page_indptr, d)
+            self.page_values = _i32(w.page_values, d)
+            self.length_info = _i32(w.length_info, d)
         elif w.kind == "ragged":
             self.k = w.k.to(d)
             self.v = w.v.to(d)
@@ -115,6 +121,11 @@ class DeviceInputs:
                 causal=w.causal, out=self.out, lse=self.lse, rotary_mode=w.rotary_mode,
                 rope_scale=w.rope_scale, rope_theta=w.rope_theta, sm_scale=w.sm_scale,
                 num_kv_splits=num_kv_splits, workspace=self.workspace, stream=stream)
+        if w.kind == "mla":
+            return ra.ra_mla_paged_prefill(self.q, self.q_indptr, self.pages, self.page_indptr,
+                                           self.page_values, self.length_info, causal=w.causal,
+                                           d_latent=w.d_latent, out=self.out, lse=self.lse,
+                                           sm_scale=w.sm_scale, stream=stream)
         if w.kind == "ragged":
             return ra.ra_ragged_prefill(self.q, self.q_indptr, self.k, self.v, self.kv_indptr,
                                         valid_len=self.valid_len, pad_mode=w.pad_mode,

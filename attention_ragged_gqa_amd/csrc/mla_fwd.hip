@@ -367,7 +367,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
     // did any row of the workgroup outgrow its reference? (one word per
     // wave, read after a barrier)
     __syncthreads();   // all waves are done with the last tile
-    if (lane == 0) votes[w] = __any(over && row_ok) ? 1 : 0;
+    const int vote = __any(over && row_ok) ? 1 : 0;   // over the whole wave
+    if (lane == 0) votes[w] = vote;
     __syncthreads();
     int any = 0;
 #pragma unroll

@@ -93,14 +93,15 @@ def test_mla_scores_outgrow_the_first_tile_fp16():
 
 
 def test_mla_scores_outgrow_the_first_tile_bf16():
-    """One late key of each sequence scaled by 60: the rows that see it score
-    it far above anything in their first tile (more than the 64 log2 units
-    bf16 P is allowed above the reference)."""
+    """The rotary part (the last 64 values, which only K reads) of one late
+    key of each sequence scaled by 150: many rows that see it score it far
+    above anything in their first tile (more than the 64 log2 units bf16 P
+    is allowed above the reference), while V keeps its N(0,1) values."""
     w = make_custom_mla(97, [40, 90], [500, 300], h_q=16, d_qk=576, d_latent=512, dtype="bf16",
                         causal=1)
     for b in range(w.batch):
         s1 = int(w.kv_store_indptr[b + 1])
-        w.k_store[s1 - 5] = (w.k_store[s1 - 5].float() * 60).to(w.k_store.dtype)
+        w.k_store[s1 - 5, 512:] = (w.k_store[s1 - 5, 512:].float() * 150).to(w.k_store.dtype)
     assert _outgrowing_rows(w, 64.0) > 0
     _check(w, "mla_outgrow_bf16")
 

@@ -32,8 +32,8 @@ __all__ = [
     "ra_merge_states",
     "ra_mla_paged_prefill",
     "ra_paged_kv_append",
-    "ra_set_workgroup_shape",
-    "ra_attn_workgroup_shape",
+    "ra_set_workgroup_waves",
+    "ra_attn_workgroup_waves",
     "ra_last_error",
 ]
 
@@ -43,7 +43,7 @@ LIB_NAME = "libragattn.so"
 EXPORTED_SYMBOLS = ("ra_tree_attn", "ra_paged_attn", "ra_ragged_prefill", "ra_paged_attn_split",
                     "ra_paged_attn_split_workspace", "ra_paged_attn_split_noalloc",
                     "ra_merge_states", "ra_mla_paged_prefill", "ra_paged_kv_append",
-                    "ra_set_workgroup_shape", "ra_attn_workgroup_shape", "ra_last_error")
+                    "ra_set_workgroup_waves", "ra_attn_workgroup_waves", "ra_last_error")
 
 RA_OK, RA_EINVAL, RA_EUNSUPPORTED, RA_EHIP = 0, -1, -2, -3
 RA_F16, RA_BF16 = 0, 1
@@ -96,10 +96,10 @@ def library() -> ctypes.CDLL:
     lib.ra_mla_paged_prefill.argtypes = [vp] * 6 + [i32, vp, vp] + [i32] * 8 + [i32, f32, vp]
     lib.ra_paged_kv_append.restype = i32
     lib.ra_paged_kv_append.argtypes = [vp] * 8 + [i32] * 7 + [i32, f32, f32, vp]
-    lib.ra_set_workgroup_shape.restype = i32
-    lib.ra_set_workgroup_shape.argtypes = [i32, i32]
-    lib.ra_attn_workgroup_shape.restype = i32
-    lib.ra_attn_workgroup_shape.argtypes = [i32] * 4 + [ctypes.POINTER(i32)] * 2
+    lib.ra_set_workgroup_waves.restype = i32
+    lib.ra_set_workgroup_waves.argtypes = [i32]
+    lib.ra_attn_workgroup_waves.restype = i32
+    lib.ra_attn_workgroup_waves.argtypes = [i32] * 4
     lib.ra_last_error.restype = ctypes.c_char_p
     lib.ra_last_error.argtypes = []
     _lib = lib
@@ -110,24 +110,20 @@ def ra_last_error() -> str:
     return library().ra_last_error().decode()
 
 
-def ra_set_workgroup_shape(waves: int, rows_per_wave: int) -> None:
+def ra_set_workgroup_waves(waves: int) -> None:
     """Fix the attention kernels' workgroup shape for later launches in this
-    process: (4, 32), (8, 32) or (4, 64) (waves, packed query rows per wave),
-    or (0, 0) to let each launch choose (the default). A tuning override;
-    results are the same either way."""
-    st = library().ra_set_workgroup_shape(int(waves), int(rows_per_wave))
+    process: 4 or 8 waves (128 or 256 packed query rows per work item), or 0
+    to let each launch choose (the default). A tuning override; results are
+    the same either way."""
+    st = library().ra_set_workgroup_waves(int(waves))
     if st != RA_OK:
         raise RagAttnError(st, ra_last_error())
 
 
-def ra_attn_workgroup_shape(total_q: int, h_q: int, h_kv: int, num_kv_splits: int = 1):
-    """(waves, rows per wave) of an attention launch of these sizes."""
-    w, r = ctypes.c_int32(0), ctypes.c_int32(0)
-    st = library().ra_attn_workgroup_shape(int(total_q), int(h_q), int(h_kv), int(num_kv_splits),
-                                           ctypes.byref(w), ctypes.byref(r))
-    if st != RA_OK:
-        raise RagAttnError(st, ra_last_error())
-    return int(w.value), int(r.value)
+def ra_attn_workgroup_waves(total_q: int, h_q: int, h_kv: int, num_kv_splits: int = 1) -> int:
+    """Waves per workgroup (4 or 8) an attention launch of these sizes uses
+    (0 for sizes the entry points reject)."""
+    return int(library().ra_attn_workgroup_waves(int(total_q), int(h_q), int(h_kv), int(num_kv_splits)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

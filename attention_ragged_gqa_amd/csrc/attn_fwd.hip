@@ -64,27 +64,21 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kStages = 2;
-// Online softmax against a fixed reference per row: P = 2^(s - m_ref) is fed
-// to the PV MFMA in the input type, so it may exceed 1 by at most 2^15 in
-// fp16 (largest value 65504); bf16 has fp32's exponent range, where 2^64
-// leaves room for the fp32 sums of O and l.
-template <bool BF>
-constexpr float kHeadroom = BF ? 64.0f : 15.0f;
+// The O rescale is skipped while a row's running maximum grows by at most
+// this much (log2 units): probabilities then stay below 2^8, and the output
+// is normalised by the sum of the same rounded P that fed the PV MFMAs.
+constexpr float kRescaleSlack = 8.0f;
 
 // First token of the work item starting at packed row row0.
 __device__ __forceinline__ int t_first_of(int row0, int g) { return row0 / g; }
 
-// NW waves per workgroup, each owning NB blocks of 32 packed query rows:
-// (NW, NB) = (4, 1) two workgroups per CU, (8, 1) one, (4, 2) one with one
-// wave per SIMD (its 64 rows' accumulators need the accumulation registers).
-// The work item is BM = 32 NB NW packed query rows, and each wave loads
-// kBN / NW rows of every K/V tile. With NB = 2 every K and V fragment a wave
-// reads from LDS feeds two MFMAs, one per row block.
-template <int NW, int NB, bool BF, int D, int LAYOUT, int MASK, bool ROPE_K>
-__global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel(AttnParams p) {
+// NW waves per workgroup (4 or 8; two or one workgroups per CU): the work
+// item is BM = 32 NW packed query rows, and each wave loads kBN / NW rows of
+// every K/V tile, so eight waves issue half the K/V loads per query row.
+template <int NW, bool BF, int D, int LAYOUT, int MASK, bool ROPE_K>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p) {
   constexpr int NT = 64 * NW;                // threads
-  constexpr int RPW = 32 * NB;               // packed query rows per wave
-  constexpr int BM = RPW * NW;               // packed query rows per work item
+  constexpr int BM = 32 * NW;                // packed query rows per work item
   constexpr int RW = kBN / NW;               // rows of a K/V tile each wave loads
   constexpr int RB = D * 2;                  // bytes per head row
   constexpr int CH = D / 8;                  // 16-byte chunks per row
@@ -108,7 +102,6 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
 
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ double inv_freq_s[D / 2];
-  __shared__ int votes[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -234,19 +227,13 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
   const __amdgpu_buffer_rsrc_t tree_rsrc = make_rsrc(tree_order_, 8L * tree_size_);
   const int k_pos0 = kp0;   // paged: RoPE position of chunk key 0
 
-  // ---- this lane's query rows: block nb holds packed row R[nb] =
-  // row0 + RPW w + 32 nb + r32 (token R / g, head kvh g + R mod g) ----
-  int t_[NB], head_[NB];
-  bool row_ok_[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int R = row0 + w * RPW + 32 * nb + r32;
-    t_[nb] = R / g;
-    head_[nb] = kvh * g + (R - t_[nb] * g);
-    row_ok_[nb] = t_[nb] < qo_len && q0 + t_[nb] >= 0 && q0 + t_[nb] < total_q_;
-  }
-  const int t_lo = (row0 + w * RPW) / g;
-  const int t_hi = min((row0 + w * RPW + RPW - 1) / g, qo_len - 1);
+  // ---- this lane's query row ----
+  const int R = row0 + w * 32 + r32;
+  const int t = R / g;
+  const int head = kvh * g + (R - t * g);
+  const bool row_ok = t < qo_len && q0 + t >= 0 && q0 + t < total_q_;
+  const int t_lo = (row0 + w * 32) / g;
+  const int t_hi = min((row0 + w * 32 + 31) / g, qo_len - 1);
   const bool wave_active = t_lo < qo_len;
 
   // Causal-or-none masks: row t sees keys [lo, lim) of the chunk (lo > 0
@@ -254,46 +241,32 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
   // them over the wave's rows for the per-tile classification.
   const bool causal = (MASK == kMaskCausal) && causal_;
   const int pad_mode = MASK == kMaskCausal ? p.pad_mode : 0;
-  int lim_[NB], lo_[NB];
+  int lim_m = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
+  int lo_m = 0;
   int kv_hi = kv_len;
   int kv_lo = 0;   // first key any row of the tile can see
   const int t_last = min((row0 + BM - 1) / g, qo_len - 1);
   if (causal) kv_hi = min(kv_len, kv_len - qo_len + t_last + 1);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int t = t_[nb];
-    lim_[nb] = causal ? min(kv_len, kv_len - qo_len + t + 1) : kv_len;
-    lo_[nb] = 0;
-    if (pad_mode == 1) {          // right padding: rows and keys below valid_len
-      const int vl = min(max(valid_m, 0), kv_len);
-      lim_[nb] = (t < valid_m) ? min(lim_[nb], vl) : 0;
-    } else if (pad_mode == 2) {   // left padding, causal: valid suffixes
-      const int vq = min(max(valid_m, 0), qo_len), vk = min(max(valid_m, 0), kv_len);
-      lo_[nb] = kv_len - vk;
-      if (t < qo_len - vq) lim_[nb] = 0;
-    }
-  }
-  if (pad_mode == 1) {
-    kv_hi = (t_first_of(row0, g) < valid_m) ? min(kv_hi, min(max(valid_m, 0), kv_len)) : 0;
-  } else if (pad_mode == 2) {
+  if (pad_mode == 1) {          // right padding: rows and keys below valid_len
+    const int vl = min(max(valid_m, 0), kv_len);
+    lim_m = (t < valid_m) ? min(lim_m, vl) : 0;
+    kv_hi = (t_first_of(row0, g) < valid_m) ? min(kv_hi, vl) : 0;
+  } else if (pad_mode == 2) {   // left padding, causal: valid suffixes
     const int vq = min(max(valid_m, 0), qo_len), vk = min(max(valid_m, 0), kv_len);
+    lo_m = kv_len - vk;
+    if (t < qo_len - vq) lim_m = 0;
     kv_lo = kv_len - vk;
     if (t_last < qo_len - vq) kv_hi = 0;   // the whole tile is padding
   }
+  const int lim = lim_m, lo = lo_m;
   int lim_lo = causal ? min(kv_len, kv_len - qo_len + t_lo + 1) : kv_len;
   int lim_hi = causal ? min(kv_len, kv_len - qo_len + t_hi + 1) : kv_len;
   int lo_min = 0, lo_max = 0;
   if (pad_mode != 0) {
     // per-wave bounds by reduction over the wave's valid rows (uniform)
-    int hmin = INT_MAX, hmax = INT_MIN, lmin = INT_MAX, lmax = INT_MIN;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bool in_seq = t_[nb] < qo_len;
-      hmin = min(hmin, in_seq ? lim_[nb] : INT_MAX);
-      hmax = max(hmax, in_seq ? lim_[nb] : INT_MIN);
-      lmin = min(lmin, in_seq ? lo_[nb] : INT_MAX);
-      lmax = max(lmax, in_seq ? lo_[nb] : INT_MIN);
-    }
+    const bool in_seq = t < qo_len;
+    int hmin = in_seq ? lim : INT_MAX, hmax = in_seq ? lim : INT_MIN;
+    int lmin = in_seq ? lo : INT_MAX, lmax = in_seq ? lo : INT_MIN;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       hmin = min(hmin, __shfl_xor(hmin, m, 64));
@@ -321,14 +294,10 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
   const int n_tiles = tile_hi - tile_lo;   // tiles this workgroup processes
   const int jbase = (tile0 + tile_lo) * kBN - kshift;   // first key of the range
 
-  // enter index of each row's tree node (selected after the prologue)
-  int enter_raw[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    enter_raw[nb] = 0;
-    if constexpr (MASK == kMaskTree)
-      enter_raw[nb] = load_i32x2(tree_rsrc, tree_base + t_[nb] + tree_len - qo_len).x;
-  }
+  // enter index of this row's tree node (selected after the prologue)
+  const int c_node = t + tree_len - qo_len;
+  int enter_raw = 0;
+  if constexpr (MASK == kMaskTree) enter_raw = load_i32x2(tree_rsrc, tree_base + c_node).x;
 
   // ---- K/V tile loads: wave w fills tile rows [RW w, RW w + RW); lane covers
   // rows RW w + RPL*i + lane/CH (i < LOADS) at physical chunk lane % CH ----
@@ -594,9 +563,8 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
 #pragma unroll
     for (int u = 0; u < TPOS; ++u) tpos[u] = load_i32(pos_rsrc, tab_pos0 + (tid + u * NT) / (D / 2));
   }
-  int my_pos[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) my_pos[nb] = rope_q_ ? load_i32(pos_rsrc, q0 + t_[nb]) : 0;
+  int my_pos = 0;
+  if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
   if (n_tiles > 0 && !kq_table) load_k_pos(jbase);
   // tree intervals of tile 0 (raw; turned into window entries when stored)
   int2 win_iv = make_int2(0, 0);
@@ -628,19 +596,16 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
     if (n_tiles > 0) load_k_regs(jbase);
   }
 
-  // ---- Q fragments: lane holds row R[nb], dims 16*s + 8*hh + [0, 8) ----
-  u32x4 qf[NB][D / 16];
+  // ---- Q fragments: lane holds row R, dims 16*s + 8*hh + [0, 8) ----
+  u32x4 qf[D / 16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
+  if (row_ok) {
+    // (token, head) row index fits in 32 bits; only the byte offset needs 64
+    const unsigned qr = static_cast<unsigned>((q0 + t) * h_q_ + head);
+    const uint16_t* qrow = q_ + static_cast<size_t>(qr) * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[nb][s] = u32x4{0, 0, 0, 0};
-    if (row_ok_[nb]) {
-      // (token, head) row index fits in 32 bits; only the byte offset needs 64
-      const unsigned qr = static_cast<unsigned>((q0 + t_[nb]) * h_q_ + head_[nb]);
-      const uint16_t* qrow = q_ + static_cast<size_t>(qr) * D + 8 * hh;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[nb][s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
-    }
+    for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s);
   }
   if constexpr (LAYOUT == kContiguous) issue_first_tile();
   if (rope_q_ | rope_k_) {
@@ -671,29 +636,22 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
     pin(win_iv.y);
     if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF)[tid] = win_entry(jbase + tid, win_iv);
   }
-  int enter_c[NB];   // INT_MIN: sees the prefix only
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    enter_c[nb] = INT_MIN;
-    if constexpr (MASK == kMaskTree) {
-      pin(enter_raw[nb]);
-      const int c_node = t_[nb] + tree_len - qo_len;
-      if (row_ok_[nb] && c_node >= 0 && c_node < tree_len) enter_c[nb] = enter_raw[nb];
-    }
+  int enter_c = INT_MIN;   // sentinel: sees the prefix only
+  if constexpr (MASK == kMaskTree) {
+    pin(enter_raw);
+    if (row_ok && c_node >= 0 && c_node < tree_len) enter_c = enter_raw;
   }
   if (kq_table) __syncthreads();   // the table is visible to every wave
   if (n_tiles > 0) rope_store_k(jbase, smem, kq_table);
   if (rope_q_) {
     if (q_table) __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-    pin(my_pos[nb]);
-    if (row_ok_[nb]) {
-      const int tr = t_[nb] - t_first + (kq_table ? kq0 : 0);
+    pin(my_pos);
+    if (row_ok) {
+      const int tr = t - t_first + (kq_table ? kq0 : 0);
       const float4* trow = reinterpret_cast<const float4*>(smem + STAGE) + tr * (D / 4);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        const u32x4 a = qf[nb][s], c2 = qf[nb][s + D / 32];
+        const u32x4 a = qf[s], c2 = qf[s + D / 32];
         // frequencies 16s + 8hh + [0, 8): one 8-entry chunk of the table row
         float cs[8], sn[8];
         if (q_table || kq_table) {
@@ -709,7 +667,7 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            rope_cos_sin(my_pos[nb], rope_scale_, inv_freq_s[16 * s + 8 * hh + e], cs[e], sn[e]);
+            rope_cos_sin(my_pos, rope_scale_, inv_freq_s[16 * s + 8 * hh + e], cs[e], sn[e]);
         }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -718,11 +676,10 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
           for (int u = 0; u < 2; ++u)
             rope_pair(cs[e + u], sn[e + u], to_f32<BF>(half_of(a, e + u)), to_f32<BF>(half_of(c2, e + u)),
                       y1[u], y2[u]);
-          qf[nb][s][e >> 1] = pack2<BF>(y1[0], y1[1]);
-          qf[nb][s + D / 32][e >> 1] = pack2<BF>(y2[0], y2[1]);
+          qf[s][e >> 1] = pack2<BF>(y1[0], y1[1]);
+          qf[s + D / 32][e >> 1] = pack2<BF>(y2[0], y2[1]);
         }
       }
-    }
     }
   }
   // (the loop's first barrier publishes the K rows, tree intervals and tile 0)
@@ -743,53 +700,34 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
     }
   }
 
-  // ---- online softmax against a fixed reference per row ----
-  // A row's reference m_ref is the maximum of its first tile with a visible
-  // key (O and l are still zero then). Later tiles add P = 2^(s - m_ref)
-  // without rescaling O; P may exceed 1 by up to kHeadroom (log2 units). If
-  // any row of the work item outgrows that, the item's tiles are processed
-  // once more with m_ref = that row's final maximum, which no score exceeds.
-  // Inside the loop O is only ever an MFMA accumulator (no vector
-  // instruction touches it), so the compiler may keep it in the
-  // accumulation registers.
-  constexpr float kHead = kHeadroom<BF>;
-  float m_ref[NB], m_seen[NB];
-  float l_run[NB];   // sum of p (float32): the log-sum-exp
-  float l_mma[NB];   // sum of p as rounded for the PV MFMA: the normaliser of O
-  f32x16 o[NB][D / 32];
+  // ---- online softmax state (row R; both half-waves carry it) ----
+  float m_run = -INFINITY;
+  float l_run = 0.f;    // sum of p (float32): the log-sum-exp
+  float l_mma = 0.f;    // sum of p as rounded for the PV MFMA: the normaliser of O
+  f32x16 o[D / 32];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_ref[nb] = -INFINITY;
-    m_seen[nb] = -INFINITY;
-  }
-  bool over = false;   // a row of this lane outgrew its reference
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   const float sc = sm_scale_log2_;
 
-  // One KV tile: S^T = K Q^T, mask, softmax, O^T += V^T P^T, for each of the
-  // wave's NB row blocks. SO: byte offset of the stage holding the tile (a
-  // compile-time constant, so that it lands in the offset field of the LDS
-  // reads).
+  // One KV tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+  // SO: byte offset of the stage holding the tile (a compile-time constant,
+  // so that it lands in the offset field of the LDS reads)
   auto compute = [&](int j0, bool masked, auto so_c) __attribute__((always_inline)) {
     constexpr int SO = decltype(so_c)::value;
     char* const sm = smem + SO;
     constexpr int twin = TREE_OFF + (SO ? WIN : 0);   // the tile's tree window
     // The two 32-key blocks alternate, so consecutive MFMAs are independent,
-    // and every K fragment is read kAhead fragments before its use: the LDS
-    // latency hides behind the MFMAs instead of stalling each one. Each
-    // fragment feeds one MFMA per row block.
+    // and every K fragment is read kAhead MFMAs before its use: the LDS
+    // latency hides behind the MFMAs instead of stalling each one.
     constexpr int NF = 2 * (D / 16);
     constexpr int kAhead = 4;
-    f32x16 sacc[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sacc[nb][0] = sacc[nb][1] = f32x16{};
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
     u32x4 kf[NF];
 #pragma unroll
     for (int t = 0; t < NF; ++t)
       kf[t] = *reinterpret_cast<const u32x4*>(sm + (t & 1) * 32 * RB + koff[t >> 1]);
 #pragma unroll
-    for (int t = 0; t < NF; ++t)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[nb][t & 1] = mma32<BF>(kf[t], qf[nb][t >> 1], sacc[nb][t & 1]);
+    for (int t = 0; t < NF; ++t) sacc[t & 1] = mma32<BF>(kf[t], qf[t >> 1], sacc[t & 1]);
     // V pieces of the first 16 keys, read behind the last MFMAs so that they
     // have arrived when the softmax of this tile reaches its first PV MFMA
     // (not with in-kernel K RoPE, whose registers are needed elsewhere)
@@ -805,93 +743,88 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
 #pragma unroll
     for (int t = 0; t < NF - kAhead; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);     // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NB * kAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     if constexpr (kVEarly) __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);   // the V reads
     if (masked) {
+      if constexpr (MASK == kMaskTree) {
+        // element r of block kb is key j0 + 32kb + 8(r/4) + 4hh + r%4; its
+        // window entry (enter, length) makes the ancestor test one unsigned
+        // compare: visible iff enter_c - enter < length
+        const unsigned ec = static_cast<unsigned>(enter_c);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (MASK == kMaskTree) {
-          // element r of block kb is key j0 + 32kb + 8(r/4) + 4hh + r%4; its
-          // window entry (enter, length) makes the ancestor test one unsigned
-          // compare: visible iff enter_c - enter < length
-          const unsigned ec = static_cast<unsigned>(enter_c[nb]);
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4* wp = reinterpret_cast<const u32x4*>(smem + twin + 8 * (32 * kb + 8 * q4 + 4 * hh));
+            const u32x4 a = wp[0], c = wp[1];
+            const unsigned ex[4] = {a[0], a[2], c[0], c[2]};
+            const unsigned ln[4] = {a[1], a[3], c[1], c[3]};
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const u32x4* wp = reinterpret_cast<const u32x4*>(smem + twin + 8 * (32 * kb + 8 * q4 + 4 * hh));
-              const u32x4 a = wp[0], c = wp[1];
-              const unsigned ex[4] = {a[0], a[2], c[0], c[2]};
-              const unsigned ln[4] = {a[1], a[3], c[1], c[3]};
-#pragma unroll
-              for (int u = 0; u < 4; ++u)
-                if (!(ec - ex[u] < ln[u])) sacc[nb][kb][4 * q4 + u] = -INFINITY;
-            }
+            for (int u = 0; u < 4; ++u)
+              if (!(ec - ex[u] < ln[u])) sacc[kb][4 * q4 + u] = -INFINITY;
           }
+        }
+      } else {
+        // key j0 + 4hh + c(kb, r) is visible iff lo - j0 - 4hh <= c < lim - j0 - 4hh
+        const int rel = lim - j0 - 4 * hh;
+        if (lo_max == 0 && j0 >= 0) {   // uniform: no lower bound (no left padding, no keys j < 0)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) sacc[kb][r] = -INFINITY;
         } else {
-          // key j0 + 4hh + c(kb, r) is visible iff lo - j0 - 4hh <= c < lim - j0 - 4hh
-          const int rel = lim_[nb] - j0 - 4 * hh;
-          if (lo_max == 0 && j0 >= 0) {   // uniform: no lower bound (no left padding, no keys j < 0)
+          const int rel_lo = lo - j0 - 4 * hh;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (32 * kb + 8 * (r >> 2) + (r & 3) >= rel) sacc[nb][kb][r] = -INFINITY;
-          } else {
-            const int rel_lo = lo_[nb] - j0 - 4 * hh;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-                if ((c >= rel) | (c < rel_lo)) sacc[nb][kb][r] = -INFINITY;
-              }
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+              if ((c >= rel) | (c < rel_lo)) sacc[kb][r] = -INFINITY;
+            }
         }
       }
     }
-    float m_use[NB];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = pair_max(mx) * sc;
+    const bool grow = mx > m_run + kRescaleSlack;   // always true while m_run = -inf
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+      l_mma *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][kb][r]);
-      mx = pair_max(mx) * sc;
-      m_seen[nb] = fmaxf(m_seen[nb], mx);
-      if (m_ref[nb] == -INFINITY) m_ref[nb] = mx;   // the row's first visible keys (or still none)
-      over |= row_ok_[nb] && mx > m_ref[nb] + kHead;
-      m_use[nb] = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
     }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float lsum = 0.f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nb][kb][r], sc, -m_use[nb]));
-          sacc[nb][kb][r] = pv;
-          lsum += pv;
-        }
-      l_run[nb] += lsum;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sc, -m_use));
+        sacc[kb][r] = pv;
+        lsum += pv;
+      }
+    l_run += lsum;
 #pragma unroll
     for (int sp = 0; sp < kBN / 16; ++sp) {
+      const f32x16& sa = sacc[sp >> 1];
       const int e0 = 8 * (sp & 1);
-      u32x4 pf[NB];
+      u32x4 pf;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const f32x16& sa = sacc[nb][sp >> 1];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pf[nb][u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
-          l_mma[nb] = add_pair<BF>(pf[nb][u], l_mma[nb]);
-        }
+      for (int u = 0; u < 4; ++u) {
+        pf[u] = pack2<BF>(sa[e0 + 2 * u], sa[e0 + 2 * u + 1]);
+        l_mma = add_pair<BF>(pf[u], l_mma);
       }
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -904,8 +837,7 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
         a[1] = __builtin_bit_cast(u32x2, lo)[1];
         a[2] = __builtin_bit_cast(u32x2, hi)[0];
         a[3] = __builtin_bit_cast(u32x2, hi)[1];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb][db] = mma32<BF>(a, pf[nb], o[nb][db]);
+        o[db] = mma32<BF>(a, pf, o[db]);
       }
     }
   };
@@ -943,127 +875,73 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
           reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_entry(j0 + kBN + tid, win_iv);
     }
   };
-#pragma unroll 1
-  for (int attempt = 0;; ++attempt) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      l_run[nb] = 0.f;
-      l_mma[nb] = 0.f;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) o[nb][i] = f32x16{};
-    }
-    over = false;
-    if (attempt > 0 && n_tiles > 0) {
-      // tile 0 once more: the buffers it used have held later tiles since
-      if constexpr (LAYOUT == kPaged) {
-        page_next = fetch_page(jbase);
-        pin(page_next);
-      }
-      issue_tile(jbase, smem);
-      load_k_pos(jbase);
-      load_k_regs(jbase);
-      if (n_tiles > 1) page_next = fetch_page(jbase + kBN);
-      if constexpr (MASK == kMaskTree) {
-        win_iv = load_i32x2(tree_rsrc, tree_base + jbase + (tid & (kBN - 1)) - tree_start);
-        pin(win_iv.x);
-        pin(win_iv.y);
-        if (tid < kBN) reinterpret_cast<int2*>(smem + TREE_OFF)[tid] = win_entry(jbase + tid, win_iv);
-      }
-      rope_store_k(jbase, smem, false);
-    }
-    for (int it = 0; it < n_tiles; it += 2) {
-      tile_step(it, std::integral_constant<int, 0>{});
-      if (it + 1 < n_tiles) tile_step(it + 1, std::integral_constant<int, STAGE>{});
-    }
-    // One tile cannot outgrow its own maximum; otherwise the waves vote.
-    if (attempt > 0 || n_tiles <= 1) break;
-    __syncthreads();   // every wave is done with its last tile
-    const int vote = __any(over) ? 1 : 0;   // over the whole wave
-    if (lane == 0) votes[w] = vote;
-    __syncthreads();
-    int any = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) any |= votes[v];
-    if (__builtin_amdgcn_readfirstlane(any) == 0) break;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) m_ref[nb] = m_seen[nb];   // no score exceeds it now
-    __syncthreads();   // every wave has read the votes
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_tiles) tile_step(it + 1, std::integral_constant<int, STAGE>{});
   }
   const int cur = (n_tiles & 1) ? STAGE : 0;   // stage after the last tile
 
-  // ---- epilogue: out = O / l (dtype), lse = m_ref + log2(l) ----
-  float l_tot[NB], inv[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    l_tot[nb] = pair_sum(l_run[nb]);
-    const float l_o = pair_sum(l_mma[nb]);
-    inv[nb] = l_o > 0.f ? 1.f / l_o : 0.f;
-  }
+  // ---- epilogue: out = O / l (dtype), lse = m + log2(l) ----
+  // O^T fragments go through LDS so that each row is stored as whole 16-byte
+  // chunks by consecutive lanes. The stage at `cur` is free: its last reads
+  // finished before the previous barrier and no load targets it.
+  const float l_tot = pair_sum(l_run);
+  const float l_o = pair_sum(l_mma);
+  const float inv = l_o > 0.f ? 1.f / l_o : 0.f;
   if (splits > 1) {
     // split-KV partial state: O / l in fp32 and the range's lse, row-major at
     // [split][row]; the merge kernel combines the ranges
+    if (row_ok) {
+      int re = row0 + 32 * w + r32;
+      pin(re);
+      const int te = re / g;
+      const size_t li = static_cast<size_t>(split) * total_q_ * h_q_ +
+                        static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
+      float* prow = p.part_out + li * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (row_ok_[nb]) {
-        int re = row0 + RPW * w + 32 * nb + r32;
-        pin(re);
-        const int te = re / g;
-        const size_t li = static_cast<size_t>(split) * total_q_ * h_q_ +
-                          static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
-        float* prow = p.part_out + li * D;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int jb = 0; jb < 4; ++jb) {
-            const float4 v = make_float4(o[nb][db][4 * jb + 0] * inv[nb], o[nb][db][4 * jb + 1] * inv[nb],
-                                         o[nb][db][4 * jb + 2] * inv[nb], o[nb][db][4 * jb + 3] * inv[nb]);
-            *reinterpret_cast<float4*>(prow + 32 * db + 8 * jb + 4 * hh) = v;
-          }
-        if (hh == 0) p.part_lse[li] = l_tot[nb] > 0.f ? m_ref[nb] + log2f(l_tot[nb]) : -INFINITY;
-      }
+        for (int jb = 0; jb < 4; ++jb) {
+          const float4 v = make_float4(o[db][4 * jb + 0] * inv, o[db][4 * jb + 1] * inv,
+                                       o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
+          *reinterpret_cast<float4*>(prow + 32 * db + 8 * jb + 4 * hh) = v;
+        }
+      if (hh == 0) p.part_lse[li] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
     }
     return;
   }
-  // O^T fragments go through LDS so that each row is stored as whole 16-byte
-  // chunks by consecutive lanes; this wave's RPW rows, same swizzle as K.
-  // When the item's rows fit one stage, the stage at `cur` is free (its last
-  // reads finished before the previous barrier and no load targets it);
-  // otherwise they need both stages, once every wave is done with the last
-  // tile.
-  char* obuf = smem + cur + (RPW * w) * RB;
-  if constexpr (NW * RPW * RB > STAGE) {
-    static_assert(NW * RPW * RB == kStages * STAGE, "the item's rows fill both stages");
+  // This wave's 32 rows, same swizzle as K. Four waves fit in the stage at
+  // `cur`; eight need both stages, once every wave is done with the last tile.
+  char* obuf = smem + cur + (32 * w) * RB;
+  if constexpr (NW == 8) {
+    static_assert(NW * 32 * RB == kStages * STAGE, "eight waves' rows fill both stages");
     __syncthreads();
-    obuf = smem + (RPW * w) * RB;
+    obuf = smem + (32 * w) * RB;
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        // dims 32db + 8jb + 4hh + [0, 4): half hh of logical chunk 4db + jb
-        u32x2 val;
-        val[0] = pack2<BF>(o[nb][db][4 * jb + 0] * inv[nb], o[nb][db][4 * jb + 1] * inv[nb]);
-        val[1] = pack2<BF>(o[nb][db][4 * jb + 2] * inv[nb], o[nb][db][4 * jb + 3] * inv[nb]);
-        const int rr = 32 * nb + r32;
-        *reinterpret_cast<u32x2*>(obuf + rr * RB + 16 * ((4 * db + jb) ^ KSWZ(rr)) + 8 * hh) = val;
-      }
-    if (row_ok_[nb] && hh == 0) {
-      // the row's (token, head) index, recomputed here rather than kept live
-      // across the loop
-      int re = row0 + RPW * w + 32 * nb + r32;
-      pin(re);
-      const int te = re / g;
-      const unsigned li = static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
-      lse_[li] = l_tot[nb] > 0.f ? m_ref[nb] + log2f(l_tot[nb]) : -INFINITY;
+    for (int jb = 0; jb < 4; ++jb) {
+      // dims 32db + 8jb + 4hh + [0, 4): half hh of logical chunk 4db + jb
+      u32x2 val;
+      val[0] = pack2<BF>(o[db][4 * jb + 0] * inv, o[db][4 * jb + 1] * inv);
+      val[1] = pack2<BF>(o[db][4 * jb + 2] * inv, o[db][4 * jb + 3] * inv);
+      *reinterpret_cast<u32x2*>(obuf + r32 * RB + 16 * ((4 * db + jb) ^ KSWZ(r32)) + 8 * hh) = val;
     }
+  if (row_ok && hh == 0) {
+    // the row's (token, head) index, recomputed here rather than kept live
+    // across the loop
+    int re = row0 + 32 * w + r32;
+    pin(re);
+    const int te = re / g;
+    const unsigned li = static_cast<unsigned>((q0 + te) * h_q_ + kvh * g + (re - te * g));
+    lse_[li] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
   }
-  // lane: chunk pc of rows lrow + RPL*i (i < RPW / RPL) of the wave's block
+  // lane: chunk pc of rows lrow + RPL*i (i < 32 / RPL) of the wave's block
 #pragma unroll
-  for (int i = 0; i < RPW / RPL; ++i) {
-    const int rr = RPL * i + lrow;                 // row within the wave's RPW
-    const int Rg = row0 + RPW * w + rr;
+  for (int i = 0; i < 32 / RPL; ++i) {
+    const int rr = RPL * i + lrow;                 // row within the wave's 32
+    const int Rg = row0 + 32 * w + rr;
     const int tg = Rg / g;
     const u32x4 val = *reinterpret_cast<const u32x4*>(obuf + rr * RB + 16 * (pc ^ KSWZ(rr)));
     if (tg < qo_len && q0 + tg < total_q_) {
@@ -1076,58 +954,54 @@ __global__ __launch_bounds__(64 * NW, NB == 2 ? 1 : 8 / NW) void attn_fwd_kernel
 #undef KSWZ
 #undef VSWZ
 
-template <int NW, int NB, bool BF, int D, int LAYOUT, int MASK>
+template <int NW, bool BF, int D, int LAYOUT, int MASK>
 void launch_r(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (p.rope_k)
-    hipLaunchKernelGGL((attn_fwd_kernel<NW, NB, BF, D, LAYOUT, MASK, true>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<NW, BF, D, LAYOUT, MASK, true>), grid, dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<NW, NB, BF, D, LAYOUT, MASK, false>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<NW, BF, D, LAYOUT, MASK, false>), grid, dim3(64 * NW), 0, stream, p);
 }
 
-template <int NW, int NB, bool BF, int D>
+template <int NW, bool BF, int D>
 void launch_d(const AttnParams& p, KvLayout layout, MaskKind mask, dim3 grid, hipStream_t stream) {
   if (layout == kContiguous) {
-    if (mask == kMaskTree) launch_r<NW, NB, BF, D, kContiguous, kMaskTree>(p, grid, stream);
-    else launch_r<NW, NB, BF, D, kContiguous, kMaskCausal>(p, grid, stream);
+    if (mask == kMaskTree) launch_r<NW, BF, D, kContiguous, kMaskTree>(p, grid, stream);
+    else launch_r<NW, BF, D, kContiguous, kMaskCausal>(p, grid, stream);
   } else {
-    if (mask == kMaskTree) launch_r<NW, NB, BF, D, kPaged, kMaskTree>(p, grid, stream);
-    else launch_r<NW, NB, BF, D, kPaged, kMaskCausal>(p, grid, stream);
+    if (mask == kMaskTree) launch_r<NW, BF, D, kPaged, kMaskTree>(p, grid, stream);
+    else launch_r<NW, BF, D, kPaged, kMaskCausal>(p, grid, stream);
   }
 }
 
-template <int NW, int NB>
-hipError_t launch_shape(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout, MaskKind mask,
-                        hipStream_t stream) {
+template <int NW>
+hipError_t launch_nw(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout, MaskKind mask,
+                     hipStream_t stream) {
   // Upper bound on the number of work items, plus slack so that the
   // XCD-contiguous mapping (8 * ceil(items / 8) blocks) always fits.
-  constexpr long bm = 32 * NW * NB;
+  constexpr long bm = 32 * NW;
   const long tiles = (static_cast<long>(p.total_q) * p.group + bm - 1) / bm + p.batch;
   long blocks = tiles * p.h_kv * (p.num_splits > 1 ? p.num_splits : 1) + 7;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks > INT_MAX) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (is_bf16) {
-    if (head_dim == 128) launch_d<NW, NB, true, 128>(p, layout, mask, grid, stream);
-    else launch_d<NW, NB, true, 64>(p, layout, mask, grid, stream);
+    if (head_dim == 128) launch_d<NW, true, 128>(p, layout, mask, grid, stream);
+    else launch_d<NW, true, 64>(p, layout, mask, grid, stream);
   } else {
-    if (head_dim == 128) launch_d<NW, NB, false, 128>(p, layout, mask, grid, stream);
-    else launch_d<NW, NB, false, 64>(p, layout, mask, grid, stream);
+    if (head_dim == 128) launch_d<NW, false, 128>(p, layout, mask, grid, stream);
+    else launch_d<NW, false, 64>(p, layout, mask, grid, stream);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Workgroup shapes: four waves of 32 rows (two workgroups per CU), eight of
-// 32 rows (one per CU, each K/V tile shared by 256 rows) or four of 64 rows
-// (one per CU, one wave per SIMD, each K/V fragment read from LDS feeding two
-// MFMAs). The 256-row shapes load each K/V tile once for twice the rows but
-// leave one workgroup per CU, so they pay off only when the 256-row items
-// cover the device's CUs at least twice; split-KV ranges are short and use
-// four waves of 32 rows. (The item count here ignores ragged tails: a lower
-// bound.)
+// Eight-wave workgroups load each K/V tile once for 256 query rows (half the
+// loads per row) but are one per CU, so they pay off only when the 256-row
+// items cover the device's CUs at least twice; split-KV ranges are short and
+// use four waves. (The item count here ignores ragged tails: a lower bound.)
 namespace {
-std::atomic<int> g_shape_override{0};   // 0: per launch, else nw * 100 + rows per wave
+std::atomic<int> g_waves_override{0};
 
 // Compute units of the current device (256 on a whole MI355X, fewer on a
 // partition of one), queried once per device; 256 when none is visible.
@@ -1152,27 +1026,20 @@ long current_cu_count() {
 }
 }  // namespace
 
-bool set_shape_override(int waves, int rows_per_wave) {
-  const bool ok = (waves == 0 && rows_per_wave == 0) || (waves == 4 && rows_per_wave == 32) ||
-                  (waves == 8 && rows_per_wave == 32) || (waves == 4 && rows_per_wave == 64);
-  if (ok) g_shape_override.store(waves * 100 + rows_per_wave, std::memory_order_relaxed);
-  return ok;
-}
+void set_waves_override(int waves) { g_waves_override.store(waves, std::memory_order_relaxed); }
 
-WgShape shape_for(const AttnParams& p) {
-  if (p.num_splits > 1) return WgShape{4, 1};
-  const int forced = g_shape_override.load(std::memory_order_relaxed);
-  if (forced != 0) return WgShape{forced / 100, (forced % 100) / 32};
-  const long items256 = (static_cast<long>(p.total_q) * p.group + 255) / 256 * p.h_kv;
-  return items256 >= 2 * current_cu_count() ? WgShape{4, 2} : WgShape{4, 1};
+int waves_per_item(const AttnParams& p) {
+  if (p.num_splits > 1) return 4;
+  const int forced = g_waves_override.load(std::memory_order_relaxed);
+  if (forced != 0) return forced;
+  const long items8 = (static_cast<long>(p.total_q) * p.group + 255) / 256 * p.h_kv;
+  return items8 >= 2 * current_cu_count() ? 8 : 4;
 }
 
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
                        MaskKind mask, hipStream_t stream) {
-  const WgShape sh = shape_for(p);
-  if (sh.nw == 8) return launch_shape<8, 1>(p, is_bf16, head_dim, layout, mask, stream);
-  if (sh.nb == 2) return launch_shape<4, 2>(p, is_bf16, head_dim, layout, mask, stream);
-  return launch_shape<4, 1>(p, is_bf16, head_dim, layout, mask, stream);
+  if (waves_per_item(p) == 8) return launch_nw<8>(p, is_bf16, head_dim, layout, mask, stream);
+  return launch_nw<4>(p, is_bf16, head_dim, layout, mask, stream);
 }
 
 }  // namespace ra

@@ -85,28 +85,22 @@ extern "C" {
 
 const char* ra_last_error(void) { return g_err; }
 
-ra_status ra_set_workgroup_shape(int32_t waves, int32_t rows_per_wave) {
-  if (!ra::set_shape_override(waves, rows_per_wave))
-    return fail(RA_EINVAL, "workgroup shape (%d waves, %d rows per wave) not built: "
-                "(0, 0) per launch, (4, 32), (8, 32) or (4, 64)", waves, rows_per_wave);
+ra_status ra_set_workgroup_waves(int32_t waves) {
+  if (waves != 0 && waves != 4 && waves != 8)
+    return fail(RA_EINVAL, "waves must be 0 (per launch), 4 or 8, got %d", waves);
+  ra::set_waves_override(waves);
   return ok();
 }
 
-ra_status ra_attn_workgroup_shape(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits,
-                                  int32_t* waves, int32_t* rows_per_wave) {
-  if (waves == nullptr || rows_per_wave == nullptr) return fail(RA_EINVAL, "waves and rows_per_wave must be non-NULL");
-  if (total_q < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0)
-    return fail(RA_EINVAL, "sizes an attention launch would reject");
+int32_t ra_attn_workgroup_waves(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits) {
+  if (total_q < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0) return 0;
   ra::AttnParams p{};
   p.total_q = total_q;
   p.h_q = h_q;
   p.h_kv = h_kv;
   p.group = h_q / h_kv;
   p.num_splits = num_kv_splits > 1 ? num_kv_splits : 0;
-  const ra::WgShape sh = ra::shape_for(p);
-  *waves = sh.nw;
-  *rows_per_wave = 32 * sh.nb;
-  return ok();
+  return ra::waves_per_item(p);
 }
 
 ra_status ra_tree_attn(const void* q, const int32_t* q_indptr, const void* k, const void* v,

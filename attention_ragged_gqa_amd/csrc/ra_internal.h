@@ -7,8 +7,8 @@
 namespace ra {
 
 // Keys per KV tile, and packed query rows per work item of a four-wave
-// workgroup of 32-row waves (the shape split-KV launches use; other launches
-// use the shape shape_for picks).
+// workgroup (4 waves x 32 rows; the split-KV launches use four waves, other
+// launches the count waves_per_item picks).
 constexpr int kBN = 64;
 constexpr int kBM = 128;
 
@@ -97,15 +97,11 @@ struct MlaParams {
 };
 
 // Launchers (attn_fwd.hip / kv_append.hip). Return the hipError_t of the launch.
-// Workgroup shape of an attention launch: nw waves of 32 nb packed query rows
-// each ((4, 1), (8, 1) or (4, 2)). set_shape_override(waves, rows_per_wave)
-// fixes it for every later launch without split-KV ((0, 0): chosen per
-// launch); false for a shape that is not built.
-struct WgShape {
-  int nw, nb;
-};
-WgShape shape_for(const AttnParams& p);
-bool set_shape_override(int waves, int rows_per_wave);
+// Waves per workgroup (4 or 8) that launch_attn uses for p: the work item is
+// 32 packed query rows per wave. set_waves_override(0 | 4 | 8) fixes it for
+// every later launch without split-KV (0: chosen per launch).
+int waves_per_item(const AttnParams& p);
+void set_waves_override(int waves);
 hipError_t launch_attn(const AttnParams& p, int is_bf16, int head_dim, KvLayout layout,
                        MaskKind mask, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int is_bf16, int head_dim, hipStream_t stream);

@@ -412,8 +412,9 @@ def main():
     ap.add_argument("--copies", type=int, default=None,
                     help="input copies cycled per graph (default: 1 for MFMA-bound workloads, "
                          "512 MiB worth for HBM-bound ones)")
-    ap.add_argument("--shape", type=int, nargs=2, default=None, metavar=("WAVES", "ROWS"),
-                    help="force the attention workgroup shape (4 32, 8 32 or 4 64); default: per launch")
+    ap.add_argument("--waves", type=int, default=None,
+                    help="force the attention workgroup shape: 4 or 8 waves of 32 query rows "
+                         "(default: chosen per launch)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -438,8 +439,8 @@ def main():
     from workloads import CONFIG_NAMES, EXTRA_NAMES, make_config, make_extra
 
     ra.library()
-    if args.shape is not None:
-        ra.ra_set_workgroup_shape(*args.shape)
+    if args.waves is not None:
+        ra.ra_set_workgroup_waves(args.waves)
     t_gen = time.perf_counter()
     w = make_extra(args.config) if args.config in EXTRA_NAMES else make_config(int(args.config))
     split = args.split
@@ -482,10 +483,10 @@ def main():
                    "launches_per_graph": r["launches_per_graph"],
                    "input_copies": copies,
                    "eager_ms_per_step": round(r["eager_ms_per_step"], 6) if r["eager_ms_per_step"] is not None else None,
-                   # the attention kernel's workgroup shape (waves, query rows per wave)
-                   "workgroup_shape": (list(ra.ra_attn_workgroup_shape(
-                       w.total_q, w.h_q, w.h_kv, split if split > 1 else (2 if split == 0 else 1)))
-                       if w.kind != "mla" else [4, 32])},
+                   # the attention kernel's workgroup shape (split-KV launches: four)
+                   "workgroup_waves": ra.ra_attn_workgroup_waves(
+                       w.total_q, w.h_q, w.h_kv, split if split > 1 else (2 if split == 0 else 1))
+                       if w.kind != "mla" else 4},
     }
     if "warm" in r:
         line["warm"] = r["warm"]

@@ -4,7 +4,7 @@
  * C ABI of libragattn.so. Every entry point launches asynchronously on the
  * caller's HIP stream, never synchronises, allocates no device memory and
  * keeps no state between calls (apart from the process-wide workgroup shape
- * that ra_set_workgroup_shape may fix, and the per-GPU scratch array of
+ * that ra_set_workgroup_waves may fix, and the per-GPU scratch array of
  * ra_paged_attn_split_noalloc). Pointers are caller-owned device memory
  * unless stated otherwise; inputs are read-only. Index arrays are int32.
  *
@@ -294,30 +294,27 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
 
 /*
  * Workgroup shape of the attention kernels (a tuning override; results do not
- * depend on it beyond rounding order, which it leaves unchanged). A work item
- * is waves * rows_per_wave packed query rows (token, head of the group); the
- * built shapes are (4, 32): two workgroups per compute unit; (8, 32): one,
- * each K/V tile shared by 256 rows; (4, 64): one, one wave per SIMD, every
- * K/V fragment read from LDS feeding the MFMAs of two 32-row blocks. The
- * setting holds for every later ra_tree_attn, ra_paged_attn and
- * ra_ragged_prefill launch in the process; (0, 0) (the default) lets each
- * launch choose: (4, 64) when its 256-row items cover the current device's
- * compute units (256 on a whole MI355X) at least twice, else (4, 32).
- * Split-KV launches always use (4, 32).
- * Errors: RA_EINVAL for a shape not listed (the setting is then unchanged).
+ * depend on it beyond rounding order, which it leaves unchanged): waves = 4
+ * or 8 fixes 4 or 8 waves of 64 per workgroup, i.e. 128 or 256 packed query
+ * rows (token, head of the group) per work item, for every later
+ * ra_tree_attn, ra_paged_attn and ra_ragged_prefill launch in the process;
+ * waves = 0 (the default) lets each launch choose: 8 when its 256-row work
+ * items cover the current device's compute units (256 on a whole MI355X)
+ * at least twice, else 4. Eight
+ * waves share each K/V tile between twice the rows (half the K/V loads per
+ * row) at one workgroup per compute unit. Split-KV launches always use 4.
+ * Errors: RA_EINVAL for any other value (the setting is then unchanged).
  */
-ra_status ra_set_workgroup_shape(int32_t waves, int32_t rows_per_wave);
+ra_status ra_set_workgroup_waves(int32_t waves);
 
 /*
- * The workgroup shape (waves, rows per wave) that an attention launch of these
- * sizes uses under the current ra_set_workgroup_shape setting; num_kv_splits
- * is the launch's split count (0 or 1: not split). Writes *waves and
- * *rows_per_wave (host pointers). Launches nothing. Errors: RA_EINVAL for
- * NULL pointers or sizes the entry points reject (total_q < 0, h_q or h_kv
- * not positive, h_q not a multiple of h_kv).
+ * Waves per workgroup (4 or 8) that an attention launch of these sizes uses
+ * under the current ra_set_workgroup_waves setting; num_kv_splits is the
+ * launch's split count (0 or 1: not split). Returns 0 for sizes the entry
+ * points reject (total_q < 0, h_q or h_kv not positive, h_q not a multiple
+ * of h_kv). Launches nothing.
  */
-ra_status ra_attn_workgroup_shape(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits,
-                                  int32_t* waves, int32_t* rows_per_wave);
+int32_t ra_attn_workgroup_waves(int32_t total_q, int32_t h_q, int32_t h_kv, int32_t num_kv_splits);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);

@@ -198,38 +198,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         ra.library()
 
 
-def test_set_workgroup_shape_validates(lib):
-    for bad in ((-1, 32), (1, 32), (4, 16), (8, 64), (16, 32), (0, 32), (4, 0)):
-        assert lib.ra_set_workgroup_shape(*bad) == ra.RA_EINVAL
-        assert "shape" in ra.ra_last_error()
-    for good in ((4, 32), (8, 32), (4, 64), (0, 0)):
-        assert lib.ra_set_workgroup_shape(*good) == ra.RA_OK
+def test_set_workgroup_waves_validates(lib):
+    for bad in (-1, 1, 2, 3, 5, 16):
+        assert lib.ra_set_workgroup_waves(bad) == ra.RA_EINVAL
+        assert "waves" in ra.ra_last_error()
+    for good in (4, 8, 0):
+        assert lib.ra_set_workgroup_waves(good) == ra.RA_OK
 
 
-def test_workgroup_shape_policy(lib):
-    """Four waves of 64 rows when the 256-row items cover the 256 CUs at
-    least twice, four of 32 otherwise and for split-KV launches; the
-    override wins; invalid sizes are refused."""
-    q = ra.ra_attn_workgroup_shape
-    assert q(1024, 32, 8) == (4, 32)             # 16 trees x 64 nodes: 128 items of 256 rows
-    assert q(11414, 32, 8) == (4, 64)            # ragged causal prefill: ~1427 items
-    assert q(32768, 64, 8) == (4, 64)            # speculative tree: 8192 items
-    assert q(16, 32, 8) == (4, 32)               # decode
-    assert q(32768, 64, 8, 4) == (4, 32)         # split-KV
-    assert q(16384, 4, 1) == (4, 32) and q(32768, 4, 1) == (4, 64)   # boundary: 256 vs 512 items
-    for bad in ((10, 6, 4), (-1, 8, 2), (10, 8, 0)):
-        with pytest.raises(ra.RagAttnError):
-            q(*bad)
+def test_workgroup_waves_policy(lib):
+    """Eight waves when the 256-row items cover the 256 CUs at least twice,
+    four otherwise and for split-KV launches; the override wins; invalid
+    sizes give 0."""
+    q = ra.ra_attn_workgroup_waves
+    assert q(1024, 32, 8) == 4              # 16 trees x 64 nodes: 128 items of 256 rows
+    assert q(11414, 32, 8) == 8             # ragged causal prefill: ~1427 items
+    assert q(32768, 64, 8) == 8             # speculative tree: 8192 items
+    assert q(16, 32, 8) == 4                # decode
+    assert q(32768, 64, 8, 4) == 4          # split-KV
+    assert q(16384, 4, 1) == 4 and q(32768, 4, 1) == 8   # boundary: 256 vs 512 items
+    assert q(10, 6, 4) == 0 and q(-1, 8, 2) == 0 and q(10, 8, 0) == 0
     try:
-        ra.ra_set_workgroup_shape(8, 32)
-        assert q(1024, 32, 8) == (8, 32) and q(32768, 64, 8, 4) == (4, 32)
-        ra.ra_set_workgroup_shape(4, 32)
-        assert q(32768, 64, 8) == (4, 32)
-        ra.ra_set_workgroup_shape(4, 64)
-        assert q(16, 32, 8) == (4, 64)
+        ra.ra_set_workgroup_waves(8)
+        assert q(1024, 32, 8) == 8 and q(32768, 64, 8, 4) == 4
+        ra.ra_set_workgroup_waves(4)
+        assert q(32768, 64, 8) == 4
     finally:
-        ra.ra_set_workgroup_shape(0, 0)
-    assert q(32768, 64, 8) == (4, 64)
+        ra.ra_set_workgroup_waves(0)
+    assert q(32768, 64, 8) == 8
 
 
 def test_mla_rejects(lib):

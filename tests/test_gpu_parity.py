@@ -250,12 +250,12 @@ def test_deterministic_and_side_stream():
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
-@pytest.mark.parametrize("shape_", [(0, 0), (8, 32), (4, 64)])
-def test_graph_replay_matches_eager(shape_, shape):
+@pytest.mark.parametrize("n_waves", [0, 8])
+def test_graph_replay_matches_eager(n_waves, waves):
     """The benchmark times HIP-graph replays of the launch: every replay, with
     eager work and synchronizations in between, must give the eager result
-    (with the per-launch workgroup shape, and with the others forced)."""
-    shape(*shape_)
+    (with the per-launch workgroup shape, and with eight waves forced)."""
+    waves(n_waves)
     for w in (make_config(1),
               make_custom_paged(32, [130, 9], [300, 40], h_q=16, h_kv=4, d=64, dtype="f16", causal=1)):
         di = DeviceInputs(w)
@@ -377,60 +377,47 @@ def test_ragged_left_padded_workload():
 
 
 # ---------------------------------------------------------------------------
-# the other workgroup shapes on the same cases: small cases choose four waves
-# of 32 rows by default and the large workloads four waves of 64 rows, so
-# each is rerun with the shapes it does not choose
+# the other workgroup shape on the same cases: small cases choose four waves
+# by default and the large workloads eight, so each is rerun with the other
 # ---------------------------------------------------------------------------
 
 @pytest.fixture
-def shape():
+def waves():
     import attention_ragged_gqa_amd as ra
 
-    def set_(waves, rows):
-        ra.ra_set_workgroup_shape(waves, rows)
+    def set_(n):
+        ra.ra_set_workgroup_waves(n)
     yield set_
-    ra.ra_set_workgroup_shape(0, 0)
+    ra.ra_set_workgroup_waves(0)
 
 
-OTHER_SHAPES = [(8, 32), (4, 64)]
-
-
-@pytest.mark.parametrize("shape_", OTHER_SHAPES)
 @pytest.mark.parametrize("case", range(len(TREE_CASES)))
-def test_tree_small_other_shapes(case, shape_, shape):
-    shape(*shape_)
+def test_tree_small_eight_waves(case, waves):
+    waves(8)
     test_tree_small(case)
 
 
-@pytest.mark.parametrize("shape_", OTHER_SHAPES)
-def test_tree_chain_and_singletons_other_shapes(shape_, shape):
-    shape(*shape_)
+def test_tree_chain_and_singletons_eight_waves(waves):
+    waves(8)
     test_tree_chain_and_singletons()
 
 
-@pytest.mark.parametrize("shape_", OTHER_SHAPES)
 @pytest.mark.parametrize("case", range(len(PAGED_CASES)))
-def test_paged_small_other_shapes(case, shape_, shape):
-    shape(*shape_)
+def test_paged_small_eight_waves(case, waves):
+    waves(8)
     test_paged_small(case)
 
 
-@pytest.mark.parametrize("shape_", OTHER_SHAPES)
 @pytest.mark.parametrize("case", sorted(RAGGED_CASES))
-def test_ragged_prefill_padded_other_shapes(case, shape_, shape):
-    shape(*shape_)
+def test_ragged_prefill_padded_eight_waves(case, waves):
+    waves(8)
     test_ragged_prefill_padded(case)
 
 
-@pytest.mark.parametrize("shape_", [(4, 32), (8, 32), (4, 64)])
 @pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
-def test_config_parity_other_shapes(k, shape_, shape):
-    """The five workloads with the workgroup shapes their launch does not
-    choose by default (four waves of 32 rows for the two tree workloads,
-    four of 64 for the three large ones)."""
-    import attention_ragged_gqa_amd as ra
-    w = _config_case(k)[0]
-    if ra.ra_attn_workgroup_shape(w.total_q, w.h_q, w.h_kv) == shape_:
-        pytest.skip("the default shape of this workload")
-    shape(*shape_)
+def test_config_parity_other_shape(k, waves):
+    """The five workloads with the workgroup shape their launch does not
+    choose by default: eight waves for the two tree workloads, four for the
+    three large ones."""
+    waves(8 if k < 2 else 4)
     test_config_parity(k)

@@ -20,19 +20,25 @@
 //    so each lane holds one query row: row max and sum are in-lane plus one
 //    v_permlane32_swap, and P converts in place into the B operand of
 //    O^T += V^T P^T (16 MFMAs of 32 dims per 16-key piece).
-//  * KV tiles of 64 keys go from HBM straight into LDS with
-//    global_load_lds_dwordx4, two stages of 72 KiB: the latent part as
-//    64 rows of 1024 bytes (one wave-wide load per row) and the rope part as
-//    64 rows of 128 bytes. With 16-byte chunks and 64 four-byte banks, a
+//  * With one wave per SIMD nothing hides a wave's own LDS latency, so the
+//    operands are read ahead explicitly: K and Q fragments four MFMAs before
+//    their use, V pieces four PV steps ahead (the first four behind the score
+//    MFMAs, so they arrive during the softmax), the order pinned with
+//    scheduling barriers (left to itself the compiler reads each operand
+//    right before its MFMA and waits for it).
+//  * KV tiles of 32 keys go from HBM straight into LDS with
+//    global_load_lds_dwordx4, two stages of 36 KiB: the latent part as
+//    32 rows of 1024 bytes (one wave-wide load per row) and the rope part as
+//    32 rows of 128 bytes. With 16-byte chunks and 64 four-byte banks, a
 //    chunk's bank group is its index mod 16 in the latent rows; logical
 //    chunk c of latent row r sits at c ^ lswz(r), lswz(r) = 4(r mod 4) +
 //    (r / 4 mod 4), which keeps both the b128 K-operand reads (16 rows, one
 //    chunk) and the ds_read_b64_tr_b16 V-operand reads (4 rows x 4 chunks)
 //    conflict-free. In the rope rows (two per 256 bytes) chunk c of row r
 //    sits at c ^ (r / 2 mod 8).
-//  * Each wave loads a 16-key block per tile: with page size 16 and a
-//    page-aligned tile grid that block is one page, so one page number per
-//    wave and tile (loaded a tile ahead). Blocks past the chunk's end or on
+//  * Each wave loads an 8-key block per tile: with page size 16 and a
+//    tile grid aligned to 32 keys that block is half a page, so one page
+//    number per wave and tile (loaded a tile ahead). Blocks past the chunk's end or on
 //    an invalid page are loaded row by row and zero-filled.
 //  * Causal tiles are classified per wave as skipped, full or partial; the
 //    softmax runs in the log2 domain with the running maximum moved (and O
@@ -286,6 +292,41 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
       }
       sacc = mma32<BF>(ck, cq, sacc);
     }
+    // V pieces of the first kVA PV steps, read behind the score MFMAs so that
+    // they have arrived when the softmax is done
+    constexpr int NV = (kTN / 16) * (kDL / 32);   // PV steps: 16-key piece sp, 32 dims db
+    constexpr int kVA = 4;
+    auto vpiece = [&](int x) __attribute__((always_inline)) -> u32x4 {
+      const int sp = x / (kDL / 32), db = x % (kDL / 32);
+      const int add = 16 * sp * kLatRB + 256 * (db >> 2);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[0][db & 3] + add));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[1][db & 3] + add));
+      u32x4 a;
+      a[0] = __builtin_bit_cast(u32x2, lo)[0];
+      a[1] = __builtin_bit_cast(u32x2, lo)[1];
+      a[2] = __builtin_bit_cast(u32x2, hi)[0];
+      a[3] = __builtin_bit_cast(u32x2, hi)[1];
+      return a;
+    };
+    u32x4 vr[kVA];
+#pragma unroll
+    for (int x = 0; x < kVA; ++x) vr[x] = vpiece(x);
+    // issue order: the first kAhead steps' reads, then each MFMA followed by
+    // the reads it made room for, then the first V reads
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead + (kAhead < kQS ? kAhead : kQS), 0);
+    static_assert(kAhead <= kQS && kQS <= NS, "read-ahead ranges");
+#pragma unroll
+    for (int x = 0; x < kQS - kAhead; ++x) {   // K and Q fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int x = kQS - kAhead; x < NS - kAhead; ++x) {   // K only
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVA, 0);
     if (masked) {
       // key j0 + 8 (r / 4) + 4 hh + r % 4 is visible iff below lim
       const int rel = lim - j0 - 4 * hh;
@@ -311,27 +352,27 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
       lsum += pv;
     }
     l_run += lsum;
+    u32x4 pf[kTN / 16];
 #pragma unroll
     for (int sp = 0; sp < kTN / 16; ++sp) {
       const int e0 = 8 * sp;
-      u32x4 pf;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        pf[u] = pack2<BF>(sacc[e0 + 2 * u], sacc[e0 + 2 * u + 1]);
-        l_mma = add_pair<BF>(pf[u], l_mma);
+        pf[sp][u] = pack2<BF>(sacc[e0 + 2 * u], sacc[e0 + 2 * u + 1]);
+        l_mma = add_pair<BF>(pf[sp][u], l_mma);
       }
+    }
+    // O^T += V^T P^T, V pieces read kVA steps ahead
 #pragma unroll
-      for (int db = 0; db < kDL / 32; ++db) {
-        const int add = 16 * sp * kLatRB + 256 * (db >> 2);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[0][db & 3] + add));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sm + voff[1][db & 3] + add));
-        u32x4 a;
-        a[0] = __builtin_bit_cast(u32x2, lo)[0];
-        a[1] = __builtin_bit_cast(u32x2, lo)[1];
-        a[2] = __builtin_bit_cast(u32x2, hi)[0];
-        a[3] = __builtin_bit_cast(u32x2, hi)[1];
-        o[db] = mma32<BF>(a, pf, o[db]);
-      }
+    for (int x = 0; x < NV; ++x) {
+      const u32x4 cv = vr[x % kVA];
+      if (x + kVA < NV) vr[x % kVA] = vpiece(x + kVA);
+      o[x % (kDL / 32)] = mma32<BF>(cv, pf[x / (kDL / 32)], o[x % (kDL / 32)]);
+    }
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (x + kVA < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 

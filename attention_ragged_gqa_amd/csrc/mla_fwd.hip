@@ -345,9 +345,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      // capped so that a row that outgrew its reference stays finite until
-      // the second attempt replaces its result
-      const float pv = __builtin_amdgcn_exp2f(fminf(fmaf(sacc[r], sc, -m_use), kHead));
+      // (a row whose scores outgrow the reference may overflow P here; the
+      // item is then computed again and this attempt's results are dropped)
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], sc, -m_use));
       sacc[r] = pv;
       lsum += pv;
     }

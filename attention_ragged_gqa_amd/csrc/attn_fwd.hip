@@ -464,9 +464,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
   };
   // The partner lanes (chunks c and c ^ CH/2 of one row) need the same 8
   // frequencies: each evaluates 4 of them and they swap the results, or,
-  // with from_tab, both read them from the (cos, sin) table of the tile's
-  // rows in the other stage (built in the prologue, row r = tile row r).
-  auto rope_store_k = [&](int j0, char* stage, bool from_tab) __attribute__((always_inline)) {
+  // with from_tab, both read them from the (cos, sin) table in the other
+  // stage (built in the prologue): row r for tile row r, or with by_pos the
+  // row of the key's position, kpos - pos_base.
+  auto rope_store_k = [&](int j0, char* stage, bool from_tab, bool by_pos, int pos_base)
+                          __attribute__((always_inline)) {
     if constexpr (ROPE_K) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
@@ -476,9 +478,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
         const bool first = lc < CH / 2;
         float cs[8], sn[8];
         if (from_tab) {
-          // frequencies 8*(lc mod CH/2) + [0, 8): one 8-entry chunk of row r
-          const float4* tc = reinterpret_cast<const float4*>(smem + STAGE) + r * (D / 4) +
-                             4 * (((lc & (CH / 2 - 1)) + r) & (D / 16 - 1));
+          // frequencies 8*(lc mod CH/2) + [0, 8): one 8-entry chunk of table
+          // row tr (keys outside the chunk, which are zero or left as they
+          // are, read a clamped row)
+          int tr = r;
+          if (by_pos) {
+            int kp = kpos[i];
+            pin(kp);
+            tr = min(max(kp - pos_base, 0), kBN - 1);
+          }
+          const float4* tc = reinterpret_cast<const float4*>(smem + STAGE) + tr * (D / 4) +
+                             4 * (((lc & (CH / 2 - 1)) + tr) & (D / 16 - 1));
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float4 x = tc[v];
@@ -565,7 +575,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
   }
   int my_pos = 0;
   if (rope_q_) my_pos = load_i32(pos_rsrc, q0 + t);
-  if (n_tiles > 0 && !kq_table) load_k_pos(jbase);
+  if (n_tiles > 0) load_k_pos(jbase);
   // tree intervals of tile 0 (raw; turned into window entries when stored)
   int2 win_iv = make_int2(0, 0);
   // Window entry of chunk key kidx from its raw (enter, exit) interval:
@@ -611,19 +621,77 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
   if (rope_q_ | rope_k_) {
     if (tid < D / 2) inv_freq_s[tid] = ifreq;
   }
-  __syncthreads();   // inv_freq is visible (the loads above are still in flight)
-
-  if (q_table || kq_table) {
-    float2* tab = reinterpret_cast<float2*>(smem + STAGE);
-    const int n_ent = (kq_table ? kBN : n_tok) * (D / 2);
+  // Position table: when every position the prologue rotates (this item's
+  // query rows and, with in-kernel K RoPE, the keys of the first tile) lies
+  // in kBN consecutive values, the table holds one row per position value
+  // from the smallest on, and rows at the same position (tree nodes at equal
+  // depth) share it. Each wave's smallest and largest position go through
+  // LDS across the barrier below.
+  __shared__ int pos_mm[2 * NW];
+  if (rope_q_) {
+    int pmin = INT_MAX, pmax = INT_MIN;
+    if (row_ok) {
+      pin(my_pos);
+      pmin = my_pos;
+      pmax = my_pos;
+    }
+    if constexpr (ROPE_K) {
+      if (n_tiles > 0) {
 #pragma unroll
-    for (int u = 0; u < TPOS; ++u) pin(tpos[u]);
+        for (int i = 0; i < LOADS; ++i) {
+          const int kidx = jbase + tile_row(i);
+          int kp = kpos[i];
+          pin(kp);
+          if (kidx >= 0 && kidx < kv_len) {
+            pmin = min(pmin, kp);
+            pmax = max(pmax, kp);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      pmin = min(pmin, __shfl_xor(pmin, m, 64));
+      pmax = max(pmax, __shfl_xor(pmax, m, 64));
+    }
+    if (lane == 0) {
+      pos_mm[2 * w] = pmin;
+      pos_mm[2 * w + 1] = pmax;
+    }
+  }
+  __syncthreads();   // inv_freq and pos_mm are visible (the loads above are still in flight)
+  int pos_base = 0, pos_rows = 0;
+  bool pos_table = false;
+  if (rope_q_) {
+    int pmin = INT_MAX, pmax = INT_MIN;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      pmin = min(pmin, pos_mm[2 * v]);
+      pmax = max(pmax, pos_mm[2 * v + 1]);
+    }
+    pos_base = __builtin_amdgcn_readfirstlane(pmin);
+    // span - 1 as an unsigned difference (no overflow for any int32 pair)
+    const unsigned span1 = static_cast<unsigned>(pmax) - static_cast<unsigned>(pmin);
+    pos_table = __builtin_amdgcn_readfirstlane((pmax >= pmin && span1 < static_cast<unsigned>(kBN)) ? 1 : 0) != 0;
+    if (pos_table) pos_rows = static_cast<int>(span1) + 1;
+  }
+  const bool row_table = !pos_table && (q_table || kq_table);   // one row per token or key
+  const bool any_table = pos_table || row_table;
+
+  if (any_table) {
+    float2* tab = reinterpret_cast<float2*>(smem + STAGE);
+    const int n_ent = (pos_table ? pos_rows : (kq_table ? kBN : n_tok)) * (D / 2);
+    if (row_table) {
+#pragma unroll
+      for (int u = 0; u < TPOS; ++u) pin(tpos[u]);
+    }
 #pragma unroll
     for (int u = 0; u < TPOS; ++u) {
       const int e = tid + u * NT;
       if (e < n_ent) {
         float cs, sn;
-        rope_cos_sin(tpos[u], rope_scale_, inv_freq_s[e % (D / 2)], cs, sn);
+        const int pos = pos_table ? pos_base + e / (D / 2) : tpos[u];
+        rope_cos_sin(pos, rope_scale_, inv_freq_s[e % (D / 2)], cs, sn);
         // 8-entry chunks of a token's row rotated by the token index, so
         // that lanes reading different tokens' chunks hit different banks
         const int te = e / (D / 2), kk = e % (D / 2);
@@ -641,20 +709,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
     pin(enter_raw);
     if (row_ok && c_node >= 0 && c_node < tree_len) enter_c = enter_raw;
   }
-  if (kq_table) __syncthreads();   // the table is visible to every wave
-  if (n_tiles > 0) rope_store_k(jbase, smem, kq_table);
+  if (any_table) __syncthreads();   // the table is visible to every wave
+  if (n_tiles > 0) rope_store_k(jbase, smem, pos_table || kq_table, pos_table, pos_base);
   if (rope_q_) {
-    if (q_table) __syncthreads();
     pin(my_pos);
     if (row_ok) {
-      const int tr = t - t_first + (kq_table ? kq0 : 0);
+      const int tr = pos_table ? my_pos - pos_base : t - t_first + (kq_table ? kq0 : 0);
       const float4* trow = reinterpret_cast<const float4*>(smem + STAGE) + tr * (D / 4);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const u32x4 a = qf[s], c2 = qf[s + D / 32];
         // frequencies 16s + 8hh + [0, 8): one 8-entry chunk of the table row
         float cs[8], sn[8];
-        if (q_table || kq_table) {
+        if (any_table) {
           const float4* tc = trow + 4 * (((2 * s + hh) + tr) & (D / 16 - 1));
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -796,14 +863,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
     mx = pair_max(mx) * sc;
     const bool grow = mx > m_run + kRescaleSlack;   // always true while m_run = -inf
     if (__any(grow)) {
+      // O is exactly zero while no row of the wave has seen a visible key
+      // (every P so far was 2^-inf): then it needs no rescale
+      const bool o_zero = !__any(m_run != -INFINITY);
       const float m_new = grow ? mx : m_run;
       // rows still without a visible key keep O = l = 0 (alpha 0, never NaN)
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
       m_run = m_new;
       l_run *= alpha;
       l_mma *= alpha;
+      if (!o_zero) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      }
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
@@ -869,7 +941,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
     cls = __builtin_amdgcn_readfirstlane(cls);
     if (wave_active && cls != 0) compute(j0, cls == 2, so_c);
     if (it + 1 < n_tiles) {
-      rope_store_k(j0 + kBN, next, false);
+      rope_store_k(j0 + kBN, next, false, false, 0);
       if constexpr (MASK == kMaskTree)
         if (tid < kBN)
           reinterpret_cast<int2*>(smem + TREE_OFF + (NSO ? WIN : 0))[tid] = win_entry(j0 + kBN + tid, win_iv);

@@ -109,6 +109,33 @@ def test_tree_small(case):
     _check(w, "tree_small[%d]" % case)
 
 
+@pytest.mark.parametrize("h_q,h_kv,span", [(16, 4, None), (4, 4, None), (16, 4, 64), (16, 4, 65)])
+def test_tree_rope_position_ranges(h_q, h_kv, span):
+    """In-kernel RoPE on q and k with positions other than node depths. The
+    kernel keeps one table row per position value when an item's query rows
+    and first key tile span at most 64 positions; otherwise one row per token
+    or key, or (one query head per KV head: 128 tokens per item) per-lane
+    angles. span None: positions scattered over 300,000 values (the
+    fallbacks); 64 and 65: every item's positions span exactly that many
+    values (nodes 0 and 1 of each tree, in every item's first key tile, hold
+    the smallest and largest)."""
+    w = make_custom_tree(40, [90, 200], h_q=h_q, h_kv=h_kv, d=128, dtype="f16", rotary_mode=1,
+                         max_children=4)
+    rng = np.random.default_rng(41)
+    if span is None:
+        w.q_rope_position = rng.integers(0, 300000, size=w.total_q).astype(np.int32)
+    else:
+        pos = []
+        for b in range(w.batch):
+            n = int(w.q_indptr[b + 1] - w.q_indptr[b])
+            base = 1000 * (b + 1)
+            p = rng.integers(base, base + span, size=n)
+            p[0], p[1] = base, base + span - 1
+            pos.append(p)
+        w.q_rope_position = np.concatenate(pos).astype(np.int32)
+    _check(w, "tree_rope_positions[h%d/%d span %s]" % (h_q, h_kv, span))
+
+
 def test_tree_chain_and_singletons():
     # a chain (causal) and a forest of singletons in one batch
     w = make_custom_tree(6, [70, 40], h_q=8, h_kv=2, d=128, dtype="bf16")

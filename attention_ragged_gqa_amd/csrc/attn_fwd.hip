@@ -610,7 +610,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_kernel(AttnParams p)
   u32x4 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
-  if (row_ok) {
+  // Rows that see no key (padding, or more queries than keys under the
+  // causal mask) are masked everywhere: their Q is never read.
+  if (row_ok && lim > lo) {
     // (token, head) row index fits in 32 bits; only the byte offset needs 64
     const unsigned qr = static_cast<unsigned>((q0 + t) * h_q_ + head);
     const uint16_t* qrow = q_ + static_cast<size_t>(qr) * D + 8 * hh;

@@ -123,6 +123,35 @@ def visible_pairs(w, seqs=None) -> int:
     return total * w.h_q
 
 
+def rows_with_keys(w, seqs=None) -> int:
+    """Query tokens with at least one visible key (of the sequences in
+    ``seqs`` only, when given), by the same row limits as visible_pairs:
+    the rows whose Q the kernels read. The others (padding, or causal rows
+    past a shorter chunk) are masked everywhere; only their zero output and
+    -inf lse are written."""
+    L = chunk_lengths(w)
+    qo = np.diff(w.q_indptr).astype(np.int64)
+    total = 0
+    for b in (range(w.batch) if seqs is None else seqs):
+        if qo[b] == 0:
+            continue
+        if w.kind == "ragged" and w.pad_mode != 0:
+            v = int(w.valid_len[b])
+            if w.pad_mode == 1:
+                total += max(0, min(v, qo[b])) if min(v, L[b]) > 0 else 0
+            else:
+                vq, vk = max(0, min(v, qo[b])), max(0, min(v, L[b]))
+                t = np.arange(qo[b] - vq, qo[b])
+                total += int(np.sum(np.minimum(L[b], L[b] - qo[b] + t + 1) - (L[b] - vk) > 0))
+            continue
+        if w.causal and not (w.kind == "tree" or w.tree_order is not None):
+            t = np.arange(qo[b])
+            total += int(np.sum(np.minimum(L[b], L[b] - qo[b] + t + 1) > 0))
+        else:   # trees (a node sees itself) and unmasked rows
+            total += int(qo[b]) if L[b] > 0 else 0
+    return total
+
+
 def flops_per_pair(w) -> float:
     """2 d_qk for the score and 2 d_v for the PV product of one unmasked
     (row, head, key) pair: 4 d, or 2 (576 + 512) for latent attention."""
@@ -131,10 +160,12 @@ def flops_per_pair(w) -> float:
 
 
 def algorithmic_bytes(w) -> int:
-    """Q and out (dtype) + every visible K/V row read once (dtype) + lse (fp32)
-    + index arrays (indptrs, tree intervals, page table entries, positions)."""
+    """Q of the rows that see a key (rows_with_keys) and out of every row
+    (dtype) + every visible K/V row read once (dtype) + lse (fp32) + index
+    arrays (indptrs, tree intervals, page table entries, positions)."""
     esz = 2
     total_q = w.total_q
+    q_rows = rows_with_keys(w)
     qo = np.diff(w.q_indptr).astype(np.int64)
     L = chunk_lengths(w)
     kv_rows = int(np.sum(np.where(qo > 0, L, 0)))
@@ -142,11 +173,11 @@ def algorithmic_bytes(w) -> int:
         v = np.asarray(w.valid_len, np.int64)
         kv_rows = int(np.sum(np.where(np.minimum(v, qo) > 0, np.clip(np.minimum(v, L), 0, None), 0)))
     if w.kind == "mla":   # q + out (latent width) + lse, one shared latent row per key
-        nbytes = total_q * w.h_q * (w.d + w.d_latent) * esz + total_q * w.h_q * 4
+        nbytes = (q_rows * w.d + total_q * w.d_latent) * w.h_q * esz + total_q * w.h_q * 4
         nbytes += kv_rows * w.d * esz
         nbytes += 4 * (w.batch + 1) * 2 + 4 * int(np.sum((L + 15) // 16)) + 4 * w.batch
         return int(nbytes)
-    nbytes = 2 * total_q * w.h_q * w.d * esz + total_q * w.h_q * 4
+    nbytes = (q_rows + total_q) * w.h_q * w.d * esz + total_q * w.h_q * 4
     nbytes += kv_rows * w.h_kv * w.d * 2 * esz
     nbytes += 4 * (w.batch + 1) * 2                       # q_indptr + kv/page indptr
     if w.kind == "tree":

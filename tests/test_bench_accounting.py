@@ -13,7 +13,9 @@ from tests.parity import out_tolerance
 from workloads import make_config, make_custom_paged, make_custom_ragged, make_custom_tree
 
 
-def _count_with_oracle(w):
+def _count_with_oracle(w, rows_only=False):
+    """Visible (row, head, key) triples from the oracle's masks, or with
+    rows_only the query tokens that see at least one key."""
     total = 0
     L = bench.chunk_lengths(w)
     for b in range(w.batch):
@@ -32,12 +34,12 @@ def _count_with_oracle(w):
             vis = oracle.tree_visible(t, rows, int(L[b]), qo)
         else:
             vis = oracle.causal_visible(rows, int(L[b]), qo, w.causal)
-        total += int(vis.sum())
-    return total * w.h_q
+        total += int(vis.any(axis=1).sum()) if rows_only else int(vis.sum())
+    return total if rows_only else total * w.h_q
 
 
-def test_visible_pairs_tree_and_causal():
-    cases = [
+def _accounting_cases():
+    return [
         make_config(0),
         make_config(1),
         make_custom_tree(1, [0, 5, 33], h_q=4, h_kv=2, d=64, dtype="f16", max_children=2),
@@ -51,9 +53,23 @@ def test_visible_pairs_tree_and_causal():
         make_custom_ragged(7, [8, 11, 4], [13, 11, 6], h_q=4, h_kv=2, d=16, dtype="f16", causal=1,
                            pad_mode=2, valid_lens=[5, 11, 0]),
         make_custom_ragged(8, [8, 20], [13, 20], h_q=4, h_kv=2, d=16, dtype="f16", causal=1),
+        make_custom_ragged(9, [9, 6], [4, 6], h_q=4, h_kv=2, d=16, dtype="f16", causal=1),   # kv < qo
     ]
-    for w in cases:
+
+
+def test_visible_pairs_tree_and_causal():
+    for w in _accounting_cases():
         assert bench.visible_pairs(w) == _count_with_oracle(w), w.name
+
+
+def test_rows_with_keys_match_oracle_masks():
+    """The Q bytes of the roofline count only rows that see a key (the
+    kernels skip the others' Q); checked against the oracle's masks."""
+    for w in _accounting_cases():
+        assert bench.rows_with_keys(w) == _count_with_oracle(w, rows_only=True), w.name
+    w = make_custom_ragged(7, [8, 11, 4], [13, 11, 6], h_q=4, h_kv=2, d=16, dtype="f16", causal=1,
+                           pad_mode=2, valid_lens=[5, 11, 0])
+    assert bench.rows_with_keys(w) == 5 + 11 + 0
 
 
 def test_sliding_config_pairs_closed_form():

@@ -20,6 +20,15 @@
 //    so each lane holds one query row: row max and sum are in-lane plus one
 //    v_permlane32_swap, and P converts in place into the B operand of
 //    O^T += V^T P^T (16 MFMAs of 32 dims per 16-key piece).
+//  * The score MFMAs are inline assembly with ordinary-register operands:
+//    O takes all 256 accumulation registers, and with the compiler's own
+//    MFMAs the score accumulator landed there too, so one O block moved out
+//    and back around every tile (80 register moves per tile). The compiler
+//    does not see these MFMAs, so the wait states before vector instructions
+//    read their results are written out (20, more than an MFMA of this shape
+//    needs); consecutive MFMAs accumulating in place, and LDS reads reusing
+//    an operand register right after its MFMA issued, need none (the
+//    compiler schedules its own MFMAs the same way).
 //  * With one wave per SIMD nothing hides a wave's own LDS latency, so the
 //    operands are read ahead explicitly: K and Q fragments four MFMAs before
 //    their use, V pieces four PV steps ahead (the first four behind the score
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
     auto qfrag = [&](int s) __attribute__((always_inline)) -> u32x4 {
       return *reinterpret_cast<const u32x4*>(smem + qoff[s & 7] + 256 * (s >> 3));
     };
-    f32x16 sacc = f32x16{};
+    f32x16 sacc;
     u32x4 kf[kAhead], qa[kAhead];
 #pragma unroll
     for (int x = 0; x < kAhead; ++x) {
@@ -290,8 +299,21 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
         kf[x % kAhead] = kfrag(x + kAhead);
         if (x + kAhead < kQS) qa[x % kAhead] = qfrag(x + kAhead);
       }
-      sacc = mma32<BF>(ck, cq, sacc);
+      // score MFMAs in ordinary registers (O fills the accumulation
+      // registers); the first starts from zero, the rest accumulate in place
+      if (x == 0) {
+        if constexpr (BF)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(ck), "v"(cq));
+        else
+          asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(ck), "v"(cq));
+      } else {
+        if constexpr (BF)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(ck), "v"(cq));
+        else
+          asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(sacc) : "v"(ck), "v"(cq));
+      }
     }
+
     // V pieces of the first kVA PV steps, read behind the score MFMAs so that
     // they have arrived when the softmax is done
     constexpr int NV = (kTN / 16) * (kDL / 32);   // PV steps: 16-key piece sp, 32 dims db
@@ -311,6 +333,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void mla_fwd_kernel(MlaParams p) {
     u32x4 vr[kVA];
 #pragma unroll
     for (int x = 0; x < kVA; ++x) vr[x] = vpiece(x);
+    // Wait states before vector instructions read the score MFMAs' results:
+    // the compiler does not see the inline MFMAs above, so it inserts none.
+    // 20 is more than an MFMA of this shape needs (and more than the
+    // compiler inserts after its own ones); stalls only add to it.
+    asm volatile("s_nop 15\n\ts_nop 3" : "+v"(sacc)::"memory");
     // issue order: the first kAhead steps' reads, then each MFMA followed by
     // the reads it made room for, then the first V reads
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead + (kAhead < kQS ? kAhead : kQS), 0);

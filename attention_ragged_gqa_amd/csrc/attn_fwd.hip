@@ -23,8 +23,10 @@
 //    each lane then holds one query row and 16 keys per 32-key block, so row
 //    max and row sum are in-lane plus one v_permlane32_swap, and the fp32
 //    accumulators convert in place into the B operand of O^T += V^T P^T.
-//  * Q stays in registers (RoPE applied on load, from a per-tile cos/sin
-//    table shared by the g heads of a token).
+//  * Q stays in registers (RoPE applied on load from a cos/sin table in
+//    LDS: one row per position value when the item's positions span at most
+//    64 values, so tree nodes at equal depth share it, else one row per
+//    token, shared by its g heads). Rows that see no key load no Q.
 //  * K and V tiles (64 keys) go from HBM straight into LDS with
 //    global_load_lds_dwordx4 (no staging registers), two stages deep, as
 //    row-major tiles whose 16-byte chunks are XOR-swizzled per row. The LDS

@@ -223,12 +223,40 @@ def kernel_name(workload: str) -> str:
     return "mla_fwd_kernel" if workload.startswith("mla") else KERNEL_NAME
 
 
+def source_code_text(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    and character literals kept), so that a comment or layout edit leaves
+    the kernel hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(kernel: str = KERNEL_NAME) -> str:
+    """Hash of the kernel's code (comments and layout excluded): a counter
+    summary in profiles/ applies while it matches."""
     src = "mla_fwd.hip" if kernel == "mla_fwd_kernel" else "attn_fwd.hip"
     h = hashlib.sha256()
     for name in (src, "device_common.h", "ra_internal.h"):
-        with open(os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(source_code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

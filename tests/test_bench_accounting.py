@@ -128,3 +128,16 @@ def test_latent_attention_accounting():
     kv = (20 + 7) * 576 * 2                     # one latent row per key of the sequences with queries
     idx = 4 * 4 * 2 + 4 * (2 + 1 + 1) + 4 * 3
     assert bench.algorithmic_bytes(w) == q_out + kv + idx
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The hash that ties profiles/ to the kernel source skips comments and
+    layout but not code or string literals."""
+    a = 'int f() { // one\n  return 1; /* two */ }\nconst char* s = "// not a comment";\n'
+    b = 'int f() {   // other words\n\n  return 1;   }\nconst char* s = "// not a comment";'
+    c = 'int f() { return 2; }\nconst char* s = "// not a comment";\n'
+    d = 'int f() { return 1; }\nconst char* s = "// changed";\n'
+    assert bench.source_code_text(a) == bench.source_code_text(b)
+    assert bench.source_code_text(a) != bench.source_code_text(c)
+    assert bench.source_code_text(a) != bench.source_code_text(d)
+    assert bench.kernel_source_hash("attn_fwd_kernel") != bench.kernel_source_hash("mla_fwd_kernel")

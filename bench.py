@@ -1,7 +1,8 @@
 """Benchmark: ragged, batched, masked GQA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k|name] [--split S]
-                    [--copies N] [--no-per-config] [--no-cpu-baseline] [--copy-calibration]
+                    [--copies N] [--no-per-config] [--no-extra] [--no-cpu-baseline]
+                    [--copy-calibration]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 one launch of the attention kernel (work partition, Q load + RoPE, K/V gather
@@ -18,7 +19,11 @@ configuration in the headline; ``--config paged_decode`` times the split-KV
 entry point (ra_paged_attn_split, one step = the attention kernel + the
 merge kernel) on a decode batch, ``--split S`` picks its split count (0:
 chosen by the library, -1: the unsplit entry point); ``--config
-ragged_left_padded`` times ra_ragged_prefill on left-padded causal prompts.
+ragged_left_padded`` times ra_ragged_prefill on left-padded causal prompts,
+``--config mla_prefill`` ra_mla_paged_prefill on the latent-attention
+prefill. Those three follow-on workloads are also timed in an
+``extra_workloads`` block of the default line (decode split with the
+library's count; ``--no-extra`` skips it).
 
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
@@ -37,7 +42,7 @@ enough for 512 MiB, twice the 256 MB Infinity Cache) that every launch reads
 its bytes from HBM; the same launch on one resident copy is reported as
 ``warm``. ``roofline.traffic`` is the HBM traffic per launch measured by
 rocprofv3 counters (profiles/<kernel>_<workload>_pmc.md), reported only while
-the kernel source is unchanged since that measurement. ``cpu_baseline`` times
+the kernel's code (comments aside) is unchanged since that measurement. ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the headline workload: whole passes of
 a small workload, else whole sequences (every row and head of each), with the
 unmasked pairs of exactly those sequences counted.
@@ -67,8 +72,13 @@ KERNEL_SOURCE = os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", "attn_fwd
 KERNEL_NAME = "attn_fwd_kernel"
 DEFAULT_CONFIG = 4                 # spec_tree_paged, the largest configuration
 COLD_FOOTPRINT = 512 << 20         # bytes of distinct inputs cycled per graph (HBM-bound)
+INFINITY_CACHE = 256 << 20         # MI355X's last-level (MALL) cache
 # steps per configuration in the per_config block (about 25-100 ms of GPU time each)
 PER_CONFIG_STEPS = {0: 2000, 1: 2000, 2: 200, 3: 200, 4: 20}
+# the follow-on workloads (split-KV decode, padded batches, latent attention),
+# timed in the same run unless --no-extra: steps each (paged_decode is split
+# with the automatic count, as its own bench line runs it)
+EXTRA_STEPS = {"paged_decode": 100, "ragged_left_padded": 100, "mla_prefill": 50}
 
 
 def log(*a):
@@ -448,11 +458,19 @@ def measure(w, steps, warmup, graph_launches, launch_kw, eager_steps, copies=Non
     return res, copies
 
 
+def timing_label(r) -> str:
+    """How the inputs of a timed run relate to the 256 MB Infinity Cache."""
+    if r["copies"] > 1:
+        return "cold (%d input copies cycled)" % r["copies"]
+    if r["bytes"] > INFINITY_CACHE:
+        return "one copy of %d MB, larger than the 256 MB Infinity Cache" % (r["bytes"] >> 20)
+    return "warm"
+
+
 def per_config_entry(w, r) -> dict:
     e = {"workload": w.name, "dtype": w.dtype, "bound": r["bound"], "frac": r["frac"],
          "ms_per_step": r["ms_per_step"], "tflops": r["tflops"], "tokens_per_s": r["tokens_per_s"],
-         "mfma_frac": r["mfma_frac"], "hbm_frac": r["hbm_frac"],
-         "timing": "cold (%d input copies cycled)" % r["copies"] if r["copies"] > 1 else "warm"}
+         "mfma_frac": r["mfma_frac"], "hbm_frac": r["hbm_frac"], "timing": timing_label(r)}
     if "warm" in r:
         e["warm"] = {k: r["warm"][k] for k in ("ms_per_step", "tflops", "hbm_frac", "mfma_frac")}
     return e
@@ -476,6 +494,8 @@ def main():
                          "(default: chosen per launch)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the headline workload")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra_workloads block (decode, padded batches, latent attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graph-launches", type=int, default=100,
@@ -541,6 +561,7 @@ def main():
         "timing": {"mode": "hip_graph_replay" if args.graph_launches > 0 else "eager",
                    "launches_per_graph": r["launches_per_graph"],
                    "input_copies": copies,
+                   "inputs": timing_label(r),
                    "eager_ms_per_step": round(r["eager_ms_per_step"], 6) if r["eager_ms_per_step"] is not None else None,
                    # the attention kernel's workgroup shape (split-KV launches: four)
                    "workgroup_waves": ra.ra_attn_workgroup_waves(
@@ -565,6 +586,25 @@ def main():
             torch.cuda.empty_cache()
         per.sort(key=lambda e: CONFIG_NAMES.index(e["workload"]) if e["workload"] in CONFIG_NAMES else 99)
         line["per_config"] = per
+
+    if not args.no_extra and not args.no_per_config:
+        extra = []
+        for name, steps in EXTRA_STEPS.items():
+            if name == args.config:
+                continue
+            t0 = time.perf_counter()
+            we = make_extra(name)
+            kw = {"num_kv_splits": 0} if name == "paged_decode" else {}
+            re_, _ = measure(we, steps, 5, args.graph_launches, kw, 0)
+            e = dict(per_config_entry(we, re_), kernel=kernel_name(name))
+            if kw:
+                e["kv_splits"] = "auto"
+            extra.append(e)
+            log("[bench] extra %s: %.5f ms/step, %s frac %.4f (%.1fs)"
+                % (we.name, re_["ms_per_step"], re_["bound"], re_["frac"], time.perf_counter() - t0))
+            del we
+            torch.cuda.empty_cache()
+        line["extra_workloads"] = extra
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

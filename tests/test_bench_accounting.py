@@ -141,3 +141,9 @@ def test_kernel_hash_ignores_comments_only():
     assert bench.source_code_text(a) != bench.source_code_text(c)
     assert bench.source_code_text(a) != bench.source_code_text(d)
     assert bench.kernel_source_hash("attn_fwd_kernel") != bench.kernel_source_hash("mla_fwd_kernel")
+
+
+def test_timing_label_by_input_footprint():
+    assert bench.timing_label({"copies": 26, "bytes": 21 << 20}) == "cold (26 input copies cycled)"
+    assert bench.timing_label({"copies": 1, "bytes": 1 << 30}).startswith("one copy of 1024 MB, larger than")
+    assert bench.timing_label({"copies": 1, "bytes": 100 << 20}) == "warm"

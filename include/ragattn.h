@@ -57,7 +57,15 @@ typedef enum {
   RA_EHIP = -3           /* a HIP launch error (message from hipGetErrorString) */
 } ra_status;
 
+/* Storage type of q, k, v, out and the caches. A caller may pass any 32-bit
+ * value: others are rejected with RA_EUNSUPPORTED. In C++ the enum has a fixed
+ * int32_t underlying type, so every such value is a valid ra_dtype there too
+ * (without one, values outside 0..1 would be out of the enum's range). */
+#ifdef __cplusplus
+typedef enum : int32_t { RA_F16 = 0, RA_BF16 = 1 } ra_dtype;
+#else
 typedef enum { RA_F16 = 0, RA_BF16 = 1 } ra_dtype;
+#endif
 
 /*
  * Batched tree attention over contiguous KV ("tree_attn.py" page: tree_attn,

@@ -250,3 +250,26 @@ def test_mla_rejects(lib):
     assert call(ptrs={"out": None}) == ra.RA_EINVAL
     assert call(total_q=(1 << 31) // 16, h_q=16) == ra.RA_EUNSUPPORTED
     assert call(batch=0, total_q=0) == ra.RA_OK
+
+
+@pytest.mark.parametrize("compiler,flags", [("gcc", ["-x", "c", "-std=c99"]), ("g++", ["-x", "c++", "-std=c++17"])])
+def test_header_from_c_and_cpp(lib, tmp_path, compiler, flags):
+    """include/ragattn.h compiles as C99 and as C++17, a program using it links
+    against libragattn.so, and its calls answer as documented."""
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_from_c.c")
+    exe = str(tmp_path / "abi")
+    libdir = os.path.dirname(ra.lib_path())
+    cmd = [compiler, *flags, "-Wall", "-Werror=implicit-function-declaration", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-x", "none",
+           "-L", libdir, "-lragattn", "-Wl,-rpath," + libdir, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    lines = run.stdout.splitlines()
+    assert lines[0] == "-1 num_splits must be in [1, 64]"
+    assert lines[1].startswith("-2 dtype 7 not supported")   # RA_EUNSUPPORTED
+    assert lines[2] == "0 "                                  # RA_OK clears the message
+    rows = 16 * 32
+    assert int(lines[3]) == (4 * rows * 128 * 4 + 255) // 256 * 256 + 4 * rows * 4
+

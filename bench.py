@@ -332,7 +332,7 @@ def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
     tflops = flops_per_pair(w) * pairs / el / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": sample, "seconds": round(el, 3), "estimated": False,
-            "cpu": _cpu_model()}
+            "cpu": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def _cpu_model() -> str:

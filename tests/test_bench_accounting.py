@@ -4,6 +4,7 @@ bench.visible_pairs uses closed forms (tree depth + 1 ancestors, causal row
 limits); here they are checked against the oracle's masks counted directly.
 """
 
+import os
 import numpy as np
 import torch
 
@@ -105,6 +106,7 @@ def test_cpu_baseline_counts_what_it_times():
     w = make_config(0)
     r = bench.cpu_baseline(w, bench.visible_pairs(w), budget_s=0.2)
     assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert r["host_cpus"] == os.cpu_count() and isinstance(r["cpu"], str)
     assert r["estimated"] is False
     w = make_custom_paged(10, [300, 200, 100], [400, 200, 900], h_q=128, h_kv=8, d=64, dtype="bf16",
                           causal=1)

@@ -366,6 +366,26 @@ def test_paged_decode_full_size_split():
         compare(out, lse, ref_out, ref_lse, label="paged_decode/%s" % splits)
 
 
+
+def test_paged_long_context():
+    """Long sequences: 64 and 33 new causal queries over 131,072 and 70,001
+    cached tokens (8,192 and 4,376 permuted pages, 2,048 and 1,094 KV tiles),
+    K rotated when cached, h 8/1 (all eight query heads on one KV head), bf16.
+    Every row, through the plain entry point and split (the library's count
+    and seven ranges); out and lse are NaN-poisoned before each launch."""
+    w = make_custom_paged(9100, [64, 33], [131072, 70001], h_q=8, h_kv=1, d=128, dtype="bf16",
+                          causal=1, store_rope="linear", rope_theta=5e5, name="long_context")
+    ref_out, ref_lse = run_oracle(w)
+    di = DeviceInputs(w)
+    for splits in (None, 0, 7):
+        say("[gpu] long context splits=%s" % splits)
+        di.poison()
+        out, lse = di.launch() if splits is None else di.launch(num_kv_splits=splits)
+        torch.cuda.synchronize()
+        d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="long context/%s" % splits)
+        say("[gpu] long context splits=%s: max|d out| %.2e max rel|d lse| %.2e" % (splits, d_out, d_lse))
+
+
 # ---------------------------------------------------------------------------
 # ragged prefill over contiguous K/V, padded batches
 # ---------------------------------------------------------------------------

@@ -60,6 +60,15 @@ def test_mla_small(case):
     _check(w, "mla_small[%d]" % case)
 
 
+def test_mla_long_context():
+    """32 and 17 new causal queries over 40,000 and 65,536 cached latent rows
+    (2,500 and 4,096 permuted pages, 1,250 and 2,048 KV tiles), 16 heads,
+    bf16, every row."""
+    w = make_custom_mla(9200, [32, 17], [40000, 65536], h_q=16, d_qk=576, d_latent=512, dtype="bf16",
+                        causal=1, name="mla_long_context")
+    _check(w, "mla long context")
+
+
 def _outgrowing_rows(w, headroom):
     """Query rows (token, head) whose maximum score exceeds the maximum over
     their first 32 keys by more than `headroom` log2 units (the case the

@@ -386,6 +386,26 @@ def test_paged_long_context():
         say("[gpu] long context splits=%s: max|d out| %.2e max rel|d lse| %.2e" % (splits, d_out, d_lse))
 
 
+
+def test_paged_tree_long_prefix():
+    """Speculative trees of 200 and 129 nodes (at most 4 children, depth at
+    most 16) over 60,000- and 33,000-token paged prefixes, q rotated inline
+    at prefix length + depth, K cached rotated, h 16/2, bf16: every row, plain
+    and with the library's split count."""
+    w = make_custom_paged(9300, [200, 129], [60200, 33129], h_q=16, h_kv=2, d=128, dtype="bf16",
+                          causal=0, tree=True, tree_max_children=4, tree_max_depth=16,
+                          store_rope="tree", rotary_mode=1, rope_theta=5e5, name="tree_long_prefix")
+    ref_out, ref_lse = run_oracle(w)
+    di = DeviceInputs(w)
+    for splits in (None, 0):
+        say("[gpu] tree long prefix splits=%s" % splits)
+        di.poison()
+        out, lse = di.launch() if splits is None else di.launch(num_kv_splits=splits)
+        torch.cuda.synchronize()
+        d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="tree long prefix/%s" % splits)
+        say("[gpu] tree long prefix splits=%s: max|d out| %.2e max rel|d lse| %.2e" % (splits, d_out, d_lse))
+
+
 # ---------------------------------------------------------------------------
 # ragged prefill over contiguous K/V, padded batches
 # ---------------------------------------------------------------------------

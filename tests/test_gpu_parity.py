@@ -437,6 +437,18 @@ def test_ragged_prefill_padded(case):
     _check(w, "ragged %s" % case)
 
 
+@pytest.mark.parametrize("pad_mode", [0, 2])
+def test_ragged_prefill_long_kv(pad_mode):
+    """Contiguous K/V over long sequences: 100 and 37 causal queries over
+    50,000 and 20,037 keys (782 and 314 KV tiles), h 32/4, bf16, plain or
+    left-padded to valid lengths of 41,000 and 9,000; every row."""
+    from workloads import make_custom_ragged
+    kw = dict(pad_mode=2, valid_lens=[41000, 9000]) if pad_mode == 2 else {}
+    w = make_custom_ragged(9400, [100, 37], [50000, 20037], h_q=32, h_kv=4, d=128, dtype="bf16",
+                           causal=1, name="ragged_long_kv", **kw)
+    _check(w, "ragged long KV pad_mode %d" % pad_mode)
+
+
 def test_ragged_left_padded_workload():
     from workloads import make_extra
     w = make_extra("ragged_left_padded")

@@ -437,6 +437,27 @@ def test_ragged_prefill_padded(case):
     _check(w, "ragged %s" % case)
 
 
+@pytest.mark.parametrize("waves", [0, 8])
+def test_many_sequences(waves):
+    """Batches beyond the item search's 64-sequence rounds: 300 paged causal
+    sequences of 0-5 queries over up to 125 keys (empty ones included) and
+    200 contiguous trees of 1-11 nodes with inline q/k RoPE; every row, with
+    the workgroup shape chosen per launch and with eight waves."""
+    import attention_ragged_gqa_amd as ra
+    rng = np.random.default_rng(9500)
+    qo = [int(x) for x in rng.integers(0, 6, size=300)]
+    stored = [q + int(rng.integers(0, 120)) for q in qo]
+    sizes = [int(x) for x in np.random.default_rng(9501).integers(1, 12, size=200)]
+    ra.ra_set_workgroup_waves(waves)
+    try:
+        _check(make_custom_paged(9500, qo, stored, h_q=8, h_kv=2, d=128, dtype="bf16", causal=1),
+               "300 paged sequences, waves %d" % waves)
+        _check(make_custom_tree(9501, sizes, h_q=8, h_kv=4, d=64, dtype="f16", rotary_mode=1),
+               "200 trees, waves %d" % waves)
+    finally:
+        ra.ra_set_workgroup_waves(0)
+
+
 @pytest.mark.parametrize("pad_mode", [0, 2])
 def test_ragged_prefill_long_kv(pad_mode):
     """Contiguous K/V over long sequences: 100 and 37 causal queries over

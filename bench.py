@@ -307,7 +307,7 @@ def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
     if w.total_q * w.h_q <= 64 * 1024:
         n, t0 = 0, time.perf_counter()
         while True:
-            run_oracle(w, pool=pool)
+            run_oracle(w, pool=pool, spread=False)
             n += 1
             el = time.perf_counter() - t0
             if el >= budget_s or n >= 50:
@@ -320,7 +320,7 @@ def cpu_baseline(w, pairs_per_pass: int, budget_s: float = 12.0) -> dict:
             if len(rows) == 0:
                 continue
             t0 = time.perf_counter()
-            run_oracle(w, rows=rows, pool=pool)
+            run_oracle(w, rows=rows, pool=pool, spread=False)
             el += time.perf_counter() - t0
             pairs += visible_pairs(w, seqs=[b])
             done += 1

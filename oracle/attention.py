@@ -28,6 +28,12 @@ Definitions followed, by page and section:
   reading is used: dims t and t + D/2 share inv_freq = theta^(-2k/D) with
   k = t mod D/2, angle = float32(pos * scale) * inv_freq.
 
+Every entry point takes an optional ``spread`` array shaped like ``out``:
+when given, it is filled with the standard deviation of v under each row's
+attention weights (``attend``). That statistic is not part of the operation;
+the parity tests use it to bound how far rounding the weights to the MFMA
+input type can move an output.
+
 Readings where the pages are silent (also listed in the design notes):
   * A row with no visible key yields out = 0 and lse = -inf.
   * A tree row whose node index c falls outside [0, tree_len) sees only the
@@ -165,27 +171,37 @@ def seq_offset(j: np.ndarray, b: int, length_info, sliding_window: int) -> np.nd
 # the attention definition
 # ----------------------------------------------------------------------------
 
-def attend(qr: np.ndarray, kr: np.ndarray, vr: np.ndarray, vis: np.ndarray, sm_scale: float):
+def attend(qr: np.ndarray, kr: np.ndarray, vr: np.ndarray, vis: np.ndarray, sm_scale: float,
+           spread: bool = False):
     """out = softmax(sm_scale * q k^T | visible) v and lse = log2 sum exp.
 
     qr [R, D], kr [L, D], vr [L, Dv] float64 (Dv = D, or the latent width
     for multi-head latent attention); vis [R, L] bool.
-    Rows with no visible key: out = 0, lse = -inf."""
+    Rows with no visible key: out = 0, lse = -inf.
+    spread: also return the standard deviation of v under each row's
+    attention weights, sqrt(sum_j w_j v_j^2 - out^2) per column (0 for rows
+    with no visible key). It is not part of the operation: parity tests use
+    it to bound the effect of rounding the weights (see tests/parity.py)."""
     R = qr.shape[0]
     out = np.zeros((R, vr.shape[1]), dtype=np.float64)
     lse = np.full(R, -np.inf, dtype=np.float64)
+    sd = np.zeros((R, vr.shape[1]), dtype=np.float64)
     if kr.shape[0] == 0 or R == 0:
-        return out, lse
+        return (out, lse, sd) if spread else (out, lse)
     s = sm_scale * (qr @ kr.T)
     s = np.where(vis, s, -np.inf)
     has = vis.any(axis=1)
     if not has.any():
-        return out, lse
+        return (out, lse, sd) if spread else (out, lse)
     m = np.max(s[has], axis=1, keepdims=True)
     p = np.exp(s[has] - m)
     denom = p.sum(axis=1, keepdims=True)
     out[has] = (p @ vr) / denom
     lse[has] = (m[:, 0] + np.log(denom[:, 0])) / LN2
+    if spread:
+        second = (p @ (vr * vr)) / denom
+        sd[has] = np.sqrt(np.maximum(second - out[has] ** 2, 0.0))
+        return out, lse, sd
     return out, lse
 
 
@@ -224,22 +240,32 @@ def _select_tokens(q_indptr, rows: Optional[np.ndarray], b: int) -> np.ndarray:
     return np.sort(r[(r >= q0) & (r < q1)] - q0)
 
 
-def _attend_sequence(qb, tok_global, qi, kseq, vseq, vis, h_q, h_kv, sm_scale, out, lse):
-    """qb [n, h_q, d] rows of this sequence; writes out/lse at tok_global.
-    Query head h reads KV head h // (h_q / h_kv)."""
+def _extra(spread):
+    """Trailing argument of _attend_sequence: the spread array when requested."""
+    return () if spread is None else (spread,)
+
+
+def _attend_sequence(qb, tok_global, qi, kseq, vseq, vis, h_q, h_kv, sm_scale, out, lse, spread=None):
+    """qb [n, h_q, d] rows of this sequence; writes out/lse (and, when given,
+    spread) at tok_global. Query head h reads KV head h // (h_q / h_kv)."""
     g = h_q // h_kv
     for kvh in range(h_kv):
         heads = slice(kvh * g, (kvh + 1) * g)
         qr = qb[:, heads, :].reshape(len(qi) * g, -1)
         vis_r = np.repeat(vis, g, axis=0)
-        o, l = attend(qr, kseq[:, kvh, :], vseq[:, kvh, :], vis_r, sm_scale)
-        out[tok_global, heads, :] = o.reshape(len(qi), g, -1)
-        lse[tok_global, heads] = l.reshape(len(qi), g)
+        if spread is None:
+            res = attend(qr, kseq[:, kvh, :], vseq[:, kvh, :], vis_r, sm_scale)
+        else:
+            res = attend(qr, kseq[:, kvh, :], vseq[:, kvh, :], vis_r, sm_scale, spread=True)
+        out[tok_global, heads, :] = res[0].reshape(len(qi), g, -1)
+        lse[tok_global, heads] = res[1].reshape(len(qi), g)
+        if spread is not None:
+            spread[tok_global, heads, :] = res[2].reshape(len(qi), g, -1)
 
 
 def tree_attn(q, q_indptr, k, v, kv_indptr, q_rope_position, mn_indptr, tree_mask,
               rotary_mode: int, rope_scale: float, rope_theta: float, sm_scale: float,
-              dtype: str, rows: Optional[np.ndarray] = None):
+              dtype: str, rows: Optional[np.ndarray] = None, spread: Optional[np.ndarray] = None):
     """Batched tree attention over contiguous KV ("tree_attn.py" page, the
     tree_attn operator and its CPU kernel).
 
@@ -275,7 +301,7 @@ def tree_attn(q, q_indptr, k, v, kv_indptr, q_rope_position, mn_indptr, tree_mas
             kb = rope(kb, pos[k0:k1], rope_theta, rope_scale, dtype)
         order = tree_mask[int(mn_indptr[b]):int(mn_indptr[b + 1])]
         vis = tree_visible(order, qi, kv_len, qo_len)
-        _attend_sequence(qb, tok, qi, kb, _f64(v[k0:k1]), vis, h_q, h_kv, sm_scale, out, lse)
+        _attend_sequence(qb, tok, qi, kb, _f64(v[k0:k1]), vis, h_q, h_kv, sm_scale, out, lse, *_extra(spread))
     return out, lse
 
 
@@ -284,7 +310,7 @@ def paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info, slidin
                tree_order=None, q_rope_position=None, k_rope_pos_offset=None,
                rotary_mode: int = 0, rope_scale: float = 1.0, rope_theta: float = 1e4,
                cache_rope_position=None, cache_rope_indptr=None,
-               rows: Optional[np.ndarray] = None):
+               rows: Optional[np.ndarray] = None, spread: Optional[np.ndarray] = None):
     """Ragged prefill / tree attention over a paged KV cache.
 
     pages [num_pages, 2, h_kv, 16, d]. The mask is the tree test when tree
@@ -336,7 +362,7 @@ def paged_attn(q, q_indptr, pages, page_indptr, page_values, length_info, slidin
             vis = tree_visible(order, qi, L, qo_len)
         else:
             vis = causal_visible(qi, L, qo_len, causal)
-        _attend_sequence(qb, tok, qi, kb, vb, vis, h_q, h_kv, sm_scale, out, lse)
+        _attend_sequence(qb, tok, qi, kb, vb, vis, h_q, h_kv, sm_scale, out, lse, *_extra(spread))
     return out, lse
 
 
@@ -368,7 +394,8 @@ def padded_visible(rows: np.ndarray, kv_len: int, qo_len: int, valid: int, pad_m
 
 
 def ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len, pad_mode: int, causal: int,
-                   sm_scale: float, rows: Optional[np.ndarray] = None):
+                   sm_scale: float, rows: Optional[np.ndarray] = None,
+                   spread: Optional[np.ndarray] = None):
     """Ragged prefill: sequence b's queries q[q_indptr[b]:q_indptr[b+1]]
     attend to k/v[kv_indptr[b]:kv_indptr[b+1]] under padded_visible.
     Returns (out [total_q, h_q, d], lse [total_q, h_q]) float64."""
@@ -390,7 +417,7 @@ def ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len, pad_mode: int, causa
         vis = padded_visible(qi, L, qo_len, valid, pad_mode, causal)
         tok = q0 + qi
         _attend_sequence(_f64(q[tok]), tok, qi, _f64(k[k0:k1]), _f64(v[k0:k1]), vis, h_q, h_kv,
-                         sm_scale, out, lse)
+                         sm_scale, out, lse, *_extra(spread))
     return out, lse
 
 
@@ -399,7 +426,8 @@ def ragged_prefill(q, q_indptr, k, v, kv_indptr, valid_len, pad_mode: int, causa
 # ----------------------------------------------------------------------------
 
 def mla_paged_attn(q, q_indptr, pages, page_indptr, page_values, last_page_len, causal: int,
-                   sm_scale: float, d_latent: int, rows: Optional[np.ndarray] = None):
+                   sm_scale: float, d_latent: int, rows: Optional[np.ndarray] = None,
+                   spread: Optional[np.ndarray] = None):
     """Multi-head latent attention prefill ("_kernel_common.py" page: AttnKind
     MLA, and _alloc_mla_qkvo_buffers, whose one combined KV tile serves as K
     over all d_qk columns and as V over the first d_latent columns; the
@@ -437,7 +465,13 @@ def mla_paged_attn(q, q_indptr, pages, page_indptr, page_values, last_page_len, 
         tok = q0 + qi
         qb = _f64(q[tok])                                                    # [n, h_q, d_qk]
         qr = qb.reshape(len(qi) * h_q, d_qk)
-        o, l = attend(qr, kv, kv[:, :d_latent], np.repeat(vis, h_q, axis=0), sm_scale)
-        out[tok] = o.reshape(len(qi), h_q, d_latent)
-        lse[tok] = l.reshape(len(qi), h_q)
+        vis_r = np.repeat(vis, h_q, axis=0)
+        if spread is None:
+            res = attend(qr, kv, kv[:, :d_latent], vis_r, sm_scale)
+        else:
+            res = attend(qr, kv, kv[:, :d_latent], vis_r, sm_scale, spread=True)
+        out[tok] = res[0].reshape(len(qi), h_q, d_latent)
+        lse[tok] = res[1].reshape(len(qi), h_q)
+        if spread is not None:
+            spread[tok] = res[2].reshape(len(qi), h_q, d_latent)
     return out, lse

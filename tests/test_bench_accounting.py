@@ -96,6 +96,18 @@ def test_out_tolerance_only_relaxes_where_dtype_cannot_hold_1e2():
     assert abs(out_tolerance(np.array([-9.0]), bf)[0] - (2.0 ** -5 + 2e-3)) < 1e-12
 
 
+def test_out_tolerance_weight_rounding_term():
+    """With the oracle's spread sigma, the bound adds 2 u sigma (u = 2^-8 in
+    bf16, 2^-11 in fp16), never going below 1e-2; a NaN spread (row not
+    evaluated) adds nothing."""
+    bf, hf = torch.bfloat16, torch.float16
+    t = out_tolerance(np.array([2.0, 0.1, 2.0]), bf, np.array([1.0, 0.5, np.nan]))
+    assert abs(t[0] - (2.0 ** -7 + 2e-3 + 2 * 2.0 ** -8 * 1.0)) < 1e-12
+    assert t[1] == 1e-2 and abs(t[2] - 1e-2) < 1e-12
+    t = out_tolerance(np.array([20.0]), hf, np.array([3.0]))
+    assert abs(t[0] - max(1e-2, 2.0 ** -7 + 2e-3 + 2 * 2.0 ** -11 * 3.0)) < 1e-12
+
+
 def test_visible_pairs_per_sequence_sum_to_total():
     for w in (make_config(1), make_custom_paged(9, [7, 40, 0, 3], [30, 40, 5, 80], h_q=4, h_kv=1, d=64,
                                                 dtype="bf16", causal=1)):

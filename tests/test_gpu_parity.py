@@ -29,7 +29,7 @@ def _gpu():
     ra.library()
 
 
-def _check(w, label, rows=None, ref=None):
+def _check(w, label, rows=None, ref=None, max_abs=None):
     say("[gpu] %s: launching (b=%d total_q=%d h=%d/%d d=%d %s)" % (label, w.batch, w.total_q, w.h_q, w.h_kv, w.d, w.dtype))
     di = DeviceInputs(w)
     di.poison()
@@ -46,6 +46,8 @@ def _check(w, label, rows=None, ref=None):
     n_rows = w.total_q if rows is None else len(rows)
     say("[gpu] %s: %d of %d query tokens compared (all heads): max|d out| %.2e  max rel|d lse| %.2e"
         % (label, n_rows, w.total_q, d_out, d_lse))
+    if max_abs is not None:
+        assert d_out <= max_abs, "%s: max |d out| %.3g above %g" % (label, d_out, max_abs)
     return di
 
 
@@ -78,8 +80,10 @@ def _config_case(k):
 
 @pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
 def test_config_parity(k):
+    """The five workloads at full size; besides the per-element bound, every
+    compared element within 1e-2 of the oracle outright."""
     w, rows, ref = _config_case(k)
-    _check(w, "config%d %s" % (k, w.name), rows=rows, ref=ref)
+    _check(w, "config%d %s" % (k, w.name), rows=rows, ref=ref, max_abs=1e-2)
 
 
 # ---------------------------------------------------------------------------
@@ -435,6 +439,27 @@ def test_ragged_prefill_padded(case):
     c = dict(RAGGED_CASES[case])
     w = make_custom_ragged(c.pop("seed"), c.pop("qo"), c.pop("kv"), **c)
     _check(w, "ragged %s" % case)
+
+
+@pytest.mark.parametrize("waves", [0, 4, 8])
+def test_large_deep_trees(waves):
+    """Trees of 1,500 and 900 nodes with at most two children (deep, spanning
+    24 and 15 KV tiles) over 500- and 100-token paged prefixes, q rotated
+    inline at prefix length + depth and K cached rotated; and contiguous
+    trees of 1,000 and 300 nodes with inline q/k RoPE. Every row, each
+    workgroup shape."""
+    import attention_ragged_gqa_amd as ra
+    ra.ra_set_workgroup_waves(waves)
+    try:
+        _check(make_custom_paged(9600, [1500, 900], [2000, 1000], h_q=16, h_kv=4, d=128, dtype="bf16",
+                                 causal=0, tree=True, tree_max_children=2, store_rope="tree",
+                                 rotary_mode=1, rope_theta=5e5),
+               "deep paged trees, waves %d" % waves)
+        _check(make_custom_tree(9601, [1000, 300], h_q=16, h_kv=2, d=128, dtype="bf16", rotary_mode=1,
+                                max_children=2),
+               "deep contiguous trees, waves %d" % waves)
+    finally:
+        ra.ra_set_workgroup_waves(0)
 
 
 @pytest.mark.parametrize("waves", [0, 8])

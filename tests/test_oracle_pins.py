@@ -119,6 +119,41 @@ def test_singleton_forest_gives_v_and_score():
             assert abs(lse[i, h] - s / math.log(2)) < 1e-12
 
 
+def test_spread_closed_forms():
+    """The spread the oracle reports for tolerances, against closed forms:
+    zero queries give equal weights over the visible keys, so the spread is
+    the population standard deviation of v over them (numpy std); a row that
+    sees one key has spread 0; paged and ragged entry points agree with the
+    same definition."""
+    rng = np.random.default_rng(12)
+    L, d = 37, 16
+    v = rng.standard_normal((L, d))
+    vis = np.ones((3, L), dtype=bool)
+    vis[1, 20:] = False                       # row 1 sees keys 0..19
+    vis[2, 1:] = False                        # row 2 sees key 0 only
+    out, _, sd = oracle.attend(np.zeros((3, d)), rng.standard_normal((L, d)), v, vis, 0.5, spread=True)
+    np.testing.assert_allclose(sd[0], v.std(axis=0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sd[1], v[:20].std(axis=0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sd[2], 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out[1], v[:20].mean(axis=0), rtol=0, atol=1e-12)
+    # the entry points fill it where they fill out, from the same weights
+    w = make_custom_tree(14, [9, 33, 1], h_q=4, h_kv=2, d=64, dtype="f16")
+    w.q = torch.zeros_like(w.q)
+    sp = np.full(w.q.shape, np.nan)
+    out_t, _ = oracle.tree_attn(w.q, w.q_indptr, w.k, w.v, w.kv_indptr, None, w.mn_indptr, w.tree_mask,
+                                0, 1.0, 1e4, w.sm_scale, w.dtype, spread=sp)
+    v64 = w.v.double().numpy()
+    order = np.asarray(w.tree_mask)
+    for r in range(w.total_q):
+        b = int(np.searchsorted(np.asarray(w.q_indptr), r, side="right") - 1)
+        k0 = int(w.kv_indptr[b])
+        mine = order[int(w.mn_indptr[b]):int(w.mn_indptr[b + 1])]
+        c = r - int(w.q_indptr[b])
+        anc = [k0 + j for j in range(len(mine)) if mine[j, 0] <= mine[c, 0] < mine[j, 1]]
+        for h in range(4):
+            np.testing.assert_allclose(sp[r, h], v64[anc, h // 2].std(axis=0), rtol=0, atol=1e-9)
+
+
 def test_lse_is_base2_logsumexp():
     w = make_custom_tree(9, [20, 31], h_q=4, h_kv=2, d=64, dtype="f16", max_children=3)
     out, lse = _tree_oracle(w)

@@ -228,15 +228,18 @@ __device__ __forceinline__ float pair_sum(float x) {
 // ---- rotary embedding ------------------------------------------------------
 // Rotate-half RoPE of the "_kernel_common.py" page (_rope): for dims k and
 // k + D/2 the angle is float32(pos * scale) * inv_freq[k] with
-// inv_freq[k] = theta^(-2k/D).
+// inv_freq[k] = theta^(-2k/D), and cos/sin are float32 values.
 //   angle = pos_f * inv_freq (float64), n = nearest integer to angle/(pi/2),
 //   r = angle - n*pi/2 with pi/2 split in two parts (|r| <= pi/4 + tiny),
 //   all in float64, so r is accurate to ~1e-16 relative even for large
-//   positions; then r is rounded to float32 and sin r, cos r come from their
-//   Taylor series in float32 (sin through r^9, cos through r^10: truncation
-//   below 2e-9 on |r| <= pi/4), and the quadrant n mod 4 swaps and negates
-//   them. Against the correctly rounded float32 cos and sin the error is
-//   below 1e-7 absolute (at most one float32 ulp away from zero crossings).
+//   positions; sin r and cos r come from their Taylor series in float64
+//   (sin through r^15, cos through r^16: the first omitted terms are below
+//   5e-17 and 3e-18 on |r| <= pi/4), the quadrant n mod 4 swaps and negates
+//   them, and each is
+//   rounded once to float32. That is the correctly rounded float32 value
+//   unless the exact one lies within a few float64 ulps of a float32
+//   rounding boundary (about 4e-9 of arguments), so rotated values match a
+//   reference that rounds float64 cos/sin the same way.
 // n is taken as an int32, which holds it while |angle| < 3e9 (any int32
 // position with scale <= 1).
 // The rotated value is evaluated in float32 as cos*x + sin*partner (two
@@ -249,35 +252,45 @@ __device__ __forceinline__ void rope_cos_sin(int pos, float scale, double inv_fr
   const double kPio2Hi = 1.5707963267948966;       // float64(pi/2)
   const double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
   const double n = rint(ang * 0.6366197723675814);  // 2/pi
-  double rd = fma(-n, kPio2Hi, ang);
-  rd = fma(-n, kPio2Lo, rd);
-  const float r = static_cast<float>(rd);
-  const float r2 = r * r;
-  // sin r = r - r^3/3! + r^5/5! - r^7/7! + r^9/9!
-  float sp = 2.7557319e-06f;                        //  1/9!
-  sp = fmaf(sp, r2, -1.9841270e-04f);               // -1/7!
-  sp = fmaf(sp, r2, 8.3333333e-03f);                //  1/5!
-  sp = fmaf(sp, r2, -1.6666667e-01f);               // -1/3!
-  const float sr = fmaf(sp * r2, r, r);
-  // cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
-  float cp = -2.7557319e-07f;                       // -1/10!
-  cp = fmaf(cp, r2, 2.4801587e-05f);                //  1/8!
-  cp = fmaf(cp, r2, -1.3888889e-03f);               // -1/6!
-  cp = fmaf(cp, r2, 4.1666668e-02f);                //  1/4!
-  cp = fmaf(cp, r2, -0.5f);                         // -1/2!
-  const float cr = fmaf(cp, r2, 1.0f);
+  double r = fma(-n, kPio2Hi, ang);
+  r = fma(-n, kPio2Lo, r);
+  const double r2 = r * r;
+  // sin r = r - r^3/3! + r^5/5! - ... - r^15/15!
+  double sp = -1.0 / 1307674368000.0;              // -1/15!
+  sp = fma(sp, r2, 1.0 / 6227020800.0);            //  1/13!
+  sp = fma(sp, r2, -1.0 / 39916800.0);             // -1/11!
+  sp = fma(sp, r2, 1.0 / 362880.0);                //  1/9!
+  sp = fma(sp, r2, -1.0 / 5040.0);                 // -1/7!
+  sp = fma(sp, r2, 1.0 / 120.0);                   //  1/5!
+  sp = fma(sp, r2, -1.0 / 6.0);                    // -1/3!
+  const double sr = fma(sp * r2, r, r);
+  // cos r = 1 - r^2/2! + r^4/4! - ... + r^16/16!
+  double cp = 1.0 / 20922789888000.0;              //  1/16!
+  cp = fma(cp, r2, -1.0 / 87178291200.0);          // -1/14!
+  cp = fma(cp, r2, 1.0 / 479001600.0);             //  1/12!
+  cp = fma(cp, r2, -1.0 / 3628800.0);              // -1/10!
+  cp = fma(cp, r2, 1.0 / 40320.0);                 //  1/8!
+  cp = fma(cp, r2, -1.0 / 720.0);                  // -1/6!
+  cp = fma(cp, r2, 1.0 / 24.0);                    //  1/4!
+  cp = fma(cp, r2, -0.5);                          // -1/2!
+  const double cr = fma(cp, r2, 1.0);
   const int q = static_cast<int>(n) & 3;
-  const float sv = (q & 1) ? cr : sr;
-  const float cv = (q & 1) ? sr : cr;
-  s = (q & 2) ? -sv : sv;
-  c = ((q + 1) & 2) ? -cv : cv;
+  const double sv = (q & 1) ? cr : sr;
+  const double cv = (q & 1) ? sr : cr;
+  s = static_cast<float>((q & 2) ? -sv : sv);
+  c = static_cast<float>(((q + 1) & 2) ? -cv : cv);
 }
 
-// y1 = cos*x1 - sin*x2 (first half), y2 = cos*x2 + sin*x1 (second half).
+// y1 = cos*x1 - sin*x2 (first half), y2 = cos*x2 + sin*x1 (second half),
+// each product rounded to float32 and then the sum: contraction into a fused
+// multiply-add is switched off here (the compiler would otherwise fuse them,
+// and the result would differ from the twice-rounded one near ties of the
+// storage-type rounding).
 __device__ __forceinline__ void rope_pair(float c, float s, float x1, float x2, float& y1,
                                           float& y2) {
-  y1 = __fsub_rn(__fmul_rn(c, x1), __fmul_rn(s, x2));
-  y2 = __fadd_rn(__fmul_rn(c, x2), __fmul_rn(s, x1));
+#pragma clang fp contract(off)
+  y1 = c * x1 - s * x2;
+  y2 = c * x2 + s * x1;
 }
 
 }  // namespace ra

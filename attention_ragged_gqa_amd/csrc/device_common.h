@@ -234,9 +234,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 //   all in float64, so r is accurate to ~1e-16 relative even for large
 //   positions; sin r and cos r come from their Taylor series in float64
 //   (sin through r^15, cos through r^16: the first omitted terms are below
-//   5e-17 and 3e-18 on |r| <= pi/4), the quadrant n mod 4 swaps and negates
-//   them, and each is
-//   rounded once to float32. That is the correctly rounded float32 value
+//   5e-17 and 3e-18 on |r| <= pi/4; summed in Estrin's scheme, which rounds
+//   differently from Horner's rule by a few float64 ulps at most), the
+//   quadrant n mod 4 swaps and negates them, and each is rounded once to
+//   float32. That is the correctly rounded float32 value
 //   unless the exact one lies within a few float64 ulps of a float32
 //   rounding boundary (about 4e-9 of arguments), so rotated values match a
 //   reference that rounds float64 cos/sin the same way.
@@ -255,24 +256,23 @@ __device__ __forceinline__ void rope_cos_sin(int pos, float scale, double inv_fr
   double r = fma(-n, kPio2Hi, ang);
   r = fma(-n, kPio2Lo, r);
   const double r2 = r * r;
-  // sin r = r - r^3/3! + r^5/5! - ... - r^15/15!
-  double sp = -1.0 / 1307674368000.0;              // -1/15!
-  sp = fma(sp, r2, 1.0 / 6227020800.0);            //  1/13!
-  sp = fma(sp, r2, -1.0 / 39916800.0);             // -1/11!
-  sp = fma(sp, r2, 1.0 / 362880.0);                //  1/9!
-  sp = fma(sp, r2, -1.0 / 5040.0);                 // -1/7!
-  sp = fma(sp, r2, 1.0 / 120.0);                   //  1/5!
-  sp = fma(sp, r2, -1.0 / 6.0);                    // -1/3!
+  // sin r = r + r^3 (-1/3! + r^2/5! - ... - r^12/15!) and
+  // cos r = 1 + r^2 (-1/2! + r^2/4! - ... + r^14/16!); the two inner
+  // polynomials in x = r^2 are evaluated in Estrin's scheme (pairs of
+  // coefficients, then x^2 and x^4), which halves the dependent chain of
+  // Horner's rule
+  const double x2 = r2 * r2, x4 = x2 * x2;
+  const double sa = fma(1.0 / 120.0, r2, -1.0 / 6.0);                  //  1/5!,  -1/3!
+  const double sb = fma(1.0 / 362880.0, r2, -1.0 / 5040.0);            //  1/9!,  -1/7!
+  const double sc = fma(1.0 / 6227020800.0, r2, -1.0 / 39916800.0);    //  1/13!, -1/11!
+  const double sd = -1.0 / 1307674368000.0;                            // -1/15!
+  const double sp = fma(fma(sd, x2, sc), x4, fma(sb, x2, sa));
   const double sr = fma(sp * r2, r, r);
-  // cos r = 1 - r^2/2! + r^4/4! - ... + r^16/16!
-  double cp = 1.0 / 20922789888000.0;              //  1/16!
-  cp = fma(cp, r2, -1.0 / 87178291200.0);          // -1/14!
-  cp = fma(cp, r2, 1.0 / 479001600.0);             //  1/12!
-  cp = fma(cp, r2, -1.0 / 3628800.0);              // -1/10!
-  cp = fma(cp, r2, 1.0 / 40320.0);                 //  1/8!
-  cp = fma(cp, r2, -1.0 / 720.0);                  // -1/6!
-  cp = fma(cp, r2, 1.0 / 24.0);                    //  1/4!
-  cp = fma(cp, r2, -0.5);                          // -1/2!
+  const double ca = fma(1.0 / 24.0, r2, -0.5);                         //  1/4!,  -1/2!
+  const double cb = fma(1.0 / 40320.0, r2, -1.0 / 720.0);              //  1/8!,  -1/6!
+  const double cc = fma(1.0 / 479001600.0, r2, -1.0 / 3628800.0);      //  1/12!, -1/10!
+  const double cd = fma(1.0 / 20922789888000.0, r2, -1.0 / 87178291200.0);   // 1/16!, -1/14!
+  const double cp = fma(fma(cd, x2, cc), x4, fma(cb, x2, ca));
   const double cr = fma(cp, r2, 1.0);
   const int q = static_cast<int>(n) & 3;
   const double sv = (q & 1) ? cr : sr;

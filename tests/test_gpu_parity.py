@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from tests.parity import DeviceInputs, compare, run_oracle, say
-from workloads import make_config, make_custom_paged, make_custom_tree
+from workloads import make_config, make_custom_paged, make_custom_ragged, make_custom_tree
 
 pytestmark = pytest.mark.gpu
 
@@ -520,6 +520,106 @@ def test_ragged_left_padded_workload():
     from workloads import make_extra
     w = make_extra("ragged_left_padded")
     _check(w, w.name)
+
+
+# ---------------------------------------------------------------------------
+# the running softmax reference moving after the first tile
+# ---------------------------------------------------------------------------
+
+_LOG2E = 1.4426950408889634
+
+
+def _reference_moves(w, slack=8.0, tile=64):
+    """How often the kernel's running row maximum would move after a row's
+    first visible 64-key tile: the kernel keeps its reference until a tile
+    raises a row's maximum more than `slack` log2 units above it, and only
+    then rescales O and l. Scores in float64 from the stored Q and K (no
+    RoPE in these cases), visibility from the oracle's own mask functions,
+    tiles on the chunk's key grid from key 0. Returns (rows that move at
+    least once, moves in all, query rows x heads)."""
+    rows_moved = n_moves = n_rows = 0
+    g = w.h_q // w.h_kv
+    for b in range(w.batch):
+        q0, q1 = int(w.q_indptr[b]), int(w.q_indptr[b + 1])
+        qo = q1 - q0
+        if w.kind == "paged":
+            kb = w.k_store[int(w.kv_store_indptr[b]):int(w.kv_store_indptr[b + 1])]
+        else:
+            kb = w.k[int(w.kv_indptr[b]):int(w.kv_indptr[b + 1])]
+        kv = kb.shape[0]
+        if qo == 0 or kv == 0:
+            continue
+        rows = np.arange(qo)
+        if w.kind == "tree" or w.tree_order is not None:
+            order = (w.tree_mask[int(w.mn_indptr[b]):int(w.mn_indptr[b + 1])] if w.kind == "tree" else
+                     w.tree_order[int(w.tree_order_indptr[b]):int(w.tree_order_indptr[b + 1])])
+            vis = oracle.tree_visible(order, rows, kv, qo)
+        else:
+            vis = oracle.causal_visible(rows, kv, qo, w.causal)
+        qf, kf = w.q[q0:q1].double().numpy(), kb.double().numpy()
+        nt = (kv + tile - 1) // tile
+        for h in range(w.h_q):
+            sc = np.where(vis, qf[:, h] @ kf[:, h // g].T * (w.sm_scale * _LOG2E), -np.inf)
+            padded = np.full((qo, nt * tile), -np.inf)
+            padded[:, :kv] = sc
+            tmax = padded.reshape(qo, nt, tile).max(axis=2)
+            ref = np.full(qo, -np.inf)
+            cnt = np.zeros(qo, np.int64)
+            for t in range(nt):
+                up = tmax[:, t] > ref + slack
+                cnt += up & np.isfinite(ref)
+                ref = np.where(up, tmax[:, t], ref)
+            rows_moved += int(np.sum(cnt > 0))
+            n_moves += int(cnt.sum())
+            n_rows += qo
+    return rows_moved, n_moves, n_rows
+
+
+def _scale_rows(x, idx, factors):
+    for i, f in zip(idx, factors):
+        x[i] = (x[i].float() * f).to(x.dtype)
+
+
+def _outgrow_case(kind, dtype):
+    """sm_scale 0.5 (scores spread over tens of log2 units) and a few late
+    keys scaled by 2-8, so row maxima jump past the reference repeatedly."""
+    if kind == "ragged_causal":
+        w = make_custom_ragged(9700, [300, 129], [700, 129], h_q=8, h_kv=2, d=128, dtype=dtype, causal=1,
+                               sm_scale=0.5, name="outgrow_ragged")
+        _scale_rows(w.k, [200, 420, 640], [2, 4, 8])
+    elif kind == "paged_causal":
+        w = make_custom_paged(9701, [200, 64], [900, 300], h_q=16, h_kv=2, d=128, dtype=dtype, causal=1,
+                              sm_scale=0.5, name="outgrow_paged")
+        _scale_rows(w.k_store, [300, 560, 880, 1150], [2, 4, 8, 6])
+    elif kind == "tree":
+        w = make_custom_tree(9702, [400, 150], h_q=8, h_kv=2, d=128, dtype=dtype, max_children=2,
+                             sm_scale=0.5, name="outgrow_tree")
+        _scale_rows(w.k, [100, 200, 300, 520], [2, 4, 8, 6])
+    else:   # paged tree over a prefix
+        w = make_custom_paged(9703, [300, 90], [800, 200], h_q=8, h_kv=1, d=128, dtype=dtype, causal=0,
+                              tree=True, tree_max_children=2, sm_scale=0.5, name="outgrow_paged_tree")
+        _scale_rows(w.k_store, [150, 400, 650, 950], [2, 4, 8, 6])
+    return w
+
+
+@pytest.mark.parametrize("waves", [0, 8])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kind", ["ragged_causal", "paged_causal", "tree", "paged_tree"])
+def test_scores_outgrow_the_reference(kind, dtype, waves):
+    """Every row against the oracle where the running reference moves after
+    the first tile (O and l rescaled, several times for some rows): with N(0,1)
+    inputs at sm_scale 1/sqrt(d) it never does in cases of this size."""
+    import attention_ragged_gqa_amd as ra
+    w = _outgrow_case(kind, dtype)
+    moved, n_moves, n_rows = _reference_moves(w)
+    say("[gpu] outgrow %s %s: reference moves on %d of %d rows (%d moves)" % (kind, dtype, moved, n_rows,
+                                                                            n_moves))
+    assert moved >= 200 and n_moves > moved, "the case no longer moves the reference"
+    ra.ra_set_workgroup_waves(waves)
+    try:
+        _check(w, "outgrow %s %s waves %d" % (kind, dtype, waves))
+    finally:
+        ra.ra_set_workgroup_waves(0)
 
 
 # ---------------------------------------------------------------------------

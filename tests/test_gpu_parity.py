@@ -622,6 +622,21 @@ def test_scores_outgrow_the_reference(kind, dtype, waves):
         ra.ra_set_workgroup_waves(0)
 
 
+@pytest.mark.parametrize("splits", [3, 0])
+@pytest.mark.parametrize("kind", ["paged_causal", "paged_tree"])
+def test_split_kv_scores_outgrow_the_reference(kind, splits):
+    """The same moving reference inside split-KV ranges (fp32 partial states
+    merged by the second kernel), three splits and the automatic count."""
+    w = _outgrow_case(kind, "bf16")
+    di = DeviceInputs(w)
+    di.poison()
+    out, lse = di.launch(num_kv_splits=splits)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = run_oracle(w)
+    d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="outgrow split %s/%d" % (kind, splits))
+    say("[gpu] outgrow split-KV %s splits=%d: max|d out| %.2e max rel|d lse| %.2e" % (kind, splits, d_out, d_lse))
+
+
 # ---------------------------------------------------------------------------
 # the other workgroup shape on the same cases: small cases choose four waves
 # by default and the large workloads eight, so each is rerun with the other

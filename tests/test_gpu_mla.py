@@ -120,3 +120,26 @@ def test_mla_prefill_workload():
     rows = np.concatenate([np.arange(int(w.q_indptr[b]) + b % 2, int(w.q_indptr[b + 1]), 2)
                            for b in range(w.batch)]).astype(np.int64)
     _check(w, "mla_prefill", rows=rows)
+
+
+def test_mla_page_pool_beyond_4gib():
+    """Every latent page past the pool's first 4 GiB (page numbers shifted by
+    233,017 pages of 18 KiB into a 4.3 GB pool); the oracle reads the same
+    rows from a compact pool. Every row."""
+    w = make_custom_mla(9820, [80, 40], [700, 300], h_q=16, d_qk=576, d_latent=512, dtype="bf16", causal=1)
+    ref = run_oracle(w)
+    di = DeviceInputs(w)
+    page_bytes = di.pages[0].numel() * di.pages.element_size()
+    off = (1 << 32) // page_bytes + 1
+    big = torch.zeros((off + di.pages.shape[0],) + tuple(di.pages.shape[1:]), dtype=di.pages.dtype,
+                      device=di.pages.device)
+    big[off:] = di.pages
+    di.pages = big
+    di.page_values = di.page_values + off
+    assert big.numel() * big.element_size() > (1 << 32)
+    say("[gpu] latent pool beyond 4 GiB: %d pages of %d bytes" % (big.shape[0], page_bytes))
+    di.poison()
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    d_out, d_lse = compare(out, lse, ref[0], ref[1], label="latent pool beyond 4 GiB")
+    say("[gpu] latent pool beyond 4 GiB: max|d out| %.2e max rel|d lse| %.2e" % (d_out, d_lse))

@@ -412,6 +412,37 @@ def test_paged_long_context():
 
 
 
+def test_page_pool_beyond_4gib():
+    """Every page of the pool past its first 4 GiB (page numbers shifted by
+    65,537 pages of 64 KiB into a 4.3 GB pool): the append kernel fills the
+    cache there (K rotated on the way in, prefix then new tokens, mid-page)
+    and attention reads it, plain, split and with a tree mask. The oracle
+    runs on the same tokens in a compact pool. Every row."""
+    import copy
+    for tree in (False, True):
+        w = make_custom_paged(9810 + tree, [100, 37], [1000, 600], h_q=16, h_kv=8, d=128, dtype="bf16",
+                              causal=0 if tree else 1, tree=tree, store_rope="tree" if tree else "linear",
+                              rotary_mode=1, rope_theta=5e5, name="pool_beyond_4gib")
+        ref_out, ref_lse = run_oracle(w)
+        page_bytes = 2 * w.h_kv * 16 * w.d * 2
+        off = (1 << 32) // page_bytes + 1
+        wb = copy.copy(w)
+        wb.page_values = w.page_values + np.int32(off)
+        wb.num_pages = w.num_pages + off
+        say("[gpu] pool beyond 4 GiB (tree %s): %d pages of %d bytes" % (tree, wb.num_pages, page_bytes))
+        di = DeviceInputs(wb)
+        assert di.pages.numel() * di.pages.element_size() > (1 << 32)
+        for splits in (None, 0):
+            di.poison()
+            out, lse = di.launch() if splits is None else di.launch(num_kv_splits=splits)
+            torch.cuda.synchronize()
+            d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="pool beyond 4 GiB/%s/%s" % (tree, splits))
+            say("[gpu] pool beyond 4 GiB tree=%s splits=%s: max|d out| %.2e max rel|d lse| %.2e"
+                % (tree, splits, d_out, d_lse))
+        del di
+        torch.cuda.empty_cache()
+
+
 def test_paged_tree_long_prefix():
     """Speculative trees of 200 and 129 nodes (at most 4 children, depth at
     most 16) over 60,000- and 33,000-token paged prefixes, q rotated inline

@@ -443,6 +443,38 @@ def test_page_pool_beyond_4gib():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kind", ["ragged", "tree"])
+def test_contiguous_kv_beyond_4gib(kind):
+    """Contiguous K/V whose every key row lies past the first 4 GiB of the K
+    and V tensors (kv_indptr shifted by 2,097,153 rows of 2 KiB; 4.3 GB
+    each): ragged causal prefill and tree attention, every row, against the
+    oracle on the compact tensors."""
+    if kind == "ragged":
+        w = make_custom_ragged(9830, [60, 17], [700, 300], h_q=16, h_kv=8, d=128, dtype="bf16", causal=1,
+                               name="kv_beyond_4gib")
+    else:
+        w = make_custom_tree(9831, [200, 65], h_q=16, h_kv=8, d=128, dtype="bf16", max_children=3,
+                             name="kv_beyond_4gib")
+    ref_out, ref_lse = run_oracle(w)
+    di = DeviceInputs(w)
+    row_bytes = w.h_kv * w.d * 2
+    pad = (1 << 32) // row_bytes + 1
+    for name in ("k", "v"):
+        t = getattr(di, name)
+        big = torch.zeros((pad + t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+        big[pad:] = t
+        setattr(di, name, big)
+    di.kv_indptr = di.kv_indptr + pad
+    say("[gpu] contiguous %s K/V beyond 4 GiB: %d rows of %d bytes" % (kind, di.k.shape[0], row_bytes))
+    di.poison()
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    d_out, d_lse = compare(out, lse, ref_out, ref_lse, label="%s K/V beyond 4 GiB" % kind)
+    say("[gpu] contiguous %s K/V beyond 4 GiB: max|d out| %.2e max rel|d lse| %.2e" % (kind, d_out, d_lse))
+    del di
+    torch.cuda.empty_cache()
+
+
 def test_paged_tree_long_prefix():
     """Speculative trees of 200 and 129 nodes (at most 4 children, depth at
     most 16) over 60,000- and 33,000-token paged prefixes, q rotated inline

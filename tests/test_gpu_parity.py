@@ -475,6 +475,46 @@ def test_contiguous_kv_beyond_4gib(kind):
     torch.cuda.empty_cache()
 
 
+def test_queries_and_outputs_beyond_4gib():
+    """Q and out rows past their tensors' first 4 GiB: a leading sequence of
+    262,145 tokens x 64 heads (16 KiB per token) over a single key pushes
+    the compared sequences' rows past 4 GiB of Q (4.3 GB) and out. Ragged
+    causal prefill; the compared rows against the oracle on the compact
+    inputs. Under the bottom-right causal mask only the leading sequence's
+    last token sees its key (out = its V row of ones, lse = 0 with q = 0);
+    the others see none (out 0, lse -inf). All NaN-poisoned before."""
+    w = make_custom_ragged(9840, [90, 33], [400, 33], h_q=64, h_kv=8, d=128, dtype="bf16", causal=1,
+                           name="q_beyond_4gib")
+    ref_out, ref_lse = run_oracle(w)
+    di = DeviceInputs(w)
+    tok_bytes = w.h_q * w.d * 2
+    pad = (1 << 32) // tok_bytes + 1
+    dev = di.q.device
+
+    def grow(t, n_front, fill):
+        big = torch.full((n_front + t.shape[0],) + tuple(t.shape[1:]), fill, dtype=t.dtype, device=dev)
+        big[n_front:] = t
+        return big
+
+    di.q = grow(di.q, pad, 0.0)
+    di.k = grow(di.k, 1, 0.0)
+    di.v = grow(di.v, 1, 1.0)           # the leading sequence's one key
+    di.out = grow(di.out, pad, float("nan"))
+    di.lse = grow(di.lse, pad, float("nan"))
+    di.q_indptr = torch.cat([torch.zeros(1, dtype=torch.int32, device=dev), di.q_indptr + pad])
+    di.kv_indptr = torch.cat([torch.zeros(1, dtype=torch.int32, device=dev), di.kv_indptr + 1])
+    say("[gpu] Q/out beyond 4 GiB: %d tokens of %d bytes" % (di.q.shape[0], tok_bytes))
+    di.poison()
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    assert torch.all(out[:pad - 1] == 0).item() and torch.all(lse[:pad - 1] == -float("inf")).item()
+    assert torch.all(out[pad - 1] == 1).item() and torch.all(lse[pad - 1] == 0).item()
+    d_out, d_lse = compare(out[pad:], lse[pad:], ref_out, ref_lse, label="Q/out beyond 4 GiB")
+    say("[gpu] Q/out beyond 4 GiB: max|d out| %.2e max rel|d lse| %.2e" % (d_out, d_lse))
+    del di, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_paged_tree_long_prefix():
     """Speculative trees of 200 and 129 nodes (at most 4 children, depth at
     most 16) over 60,000- and 33,000-token paged prefixes, q rotated inline

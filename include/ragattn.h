@@ -83,8 +83,11 @@ typedef enum { RA_F16 = 0, RA_BF16 = 1 } ra_dtype;
  *   r at position q_rope_position[r] and K row r at q_rope_position[r] (the
  *   page's kernels index K positions with the same array; KV rows and query
  *   rows coincide in this operator). Angles: float32(pos * rope_scale) *
- *   rope_theta^(-2k/head_dim) for dims k and k + head_dim/2; rotated values are
- *   evaluated in float32 and rounded to dtype.
+ *   rope_theta^(-2k/head_dim) for dims k and k + head_dim/2 (the product in
+ *   float64); cos and sin are their float32 values (rounded once from a
+ *   float64 evaluation), and a rotated value is the float32 sum of two
+ *   float32 products, cos*x -/+ sin*partner (no fused multiply-add),
+ *   rounded to dtype (to nearest, ties to even).
  * q_rope_position may be NULL when rotary_mode == 0.
  * tree_size = mn_indptr[batch] (rows of tree_mask); total_kv = kv_indptr[batch].
  * Supported: head_dim 64 or 128, dtype fp16/bf16, any h_q divisible by h_kv.

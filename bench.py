@@ -23,7 +23,11 @@ ragged_left_padded`` times ra_ragged_prefill on left-padded causal prompts,
 ``--config mla_prefill`` ra_mla_paged_prefill on the latent-attention
 prefill. Those three follow-on workloads are also timed in an
 ``extra_workloads`` block of the default line (decode split with the
-library's count; ``--no-extra`` skips it).
+library's count; ``--no-extra`` skips it), and so is the step before the
+path, ``kv_append``: ra_paged_kv_append writing the headline's 32,768 new
+tree tokens (K rotated at prefix + depth) into its paged cache, HBM-bound,
+counted as each new K/V row read once and written once (``--config
+kv_append`` prints a line of its own in GB/s).
 
 Prints ONE JSON line on stdout. value = TFLOP/s counted on unmasked
 (query row, head, key) pairs only, 4*d flops each (QK^T and PV); also
@@ -79,6 +83,11 @@ PER_CONFIG_STEPS = {0: 2000, 1: 2000, 2: 200, 3: 200, 4: 20}
 # timed in the same run unless --no-extra: steps each (paged_decode is split
 # with the automatic count, as its own bench line runs it)
 EXTRA_STEPS = {"paged_decode": 100, "ragged_left_padded": 100, "mla_prefill": 50}
+# the step before the path: appending the headline's new tokens (its tree
+# nodes, K rotated at their cache positions) into its paged cache
+APPEND_NAME = "kv_append"
+APPEND_SOURCE = DEFAULT_CONFIG
+APPEND_STEPS = 100
 
 
 def log(*a):
@@ -203,6 +212,97 @@ def algorithmic_bytes(w) -> int:
     return int(nbytes)
 
 
+def append_bytes(ai) -> int:
+    """Algorithmic bytes of one append (AppendInputs ai): every new token's K
+    and V rows read once and written once into their page slots (dtype), its
+    cache position (int32), the append indptr and starts and the page indptr
+    (int32), and the page-table entries the new tokens land on."""
+    w = ai.w
+    row = w.h_kv * w.d * 2
+    n = ai.n_tokens
+    pages = sum(int((s0 + n0 - 1) // 16 - s0 // 16 + 1) for s0, n0 in zip(ai.new_start, ai.new_len) if n0 > 0)
+    return int(2 * 2 * n * row + 4 * n + 4 * (w.batch + 1) + 4 * w.batch + 4 * (w.batch + 1) + 4 * pages)
+
+
+def append_summary(ai) -> dict:
+    w = ai.w
+    starts = np.asarray(ai.new_start)
+    pos = np.asarray(w.store_rope_position)
+    return {"workload": APPEND_NAME, "source": "%s (the new tokens of each sequence)" % w.name,
+            "batch": w.batch, "tokens": ai.n_tokens, "h_kv": w.h_kv, "head_dim": w.d,
+            "kv_layout": "paged16", "num_pages": w.num_pages,
+            "rope": "K rotated on the way in, theta=%g" % w.rope_theta,
+            "positions_range": [int(pos.min()), int(pos.max())] if pos.size else [0, 0],
+            "mid_page_starts": int(np.sum(starts % 16 != 0))}
+
+
+def measure_append(w, steps, warmup, graph_launches, copies=None):
+    """Time the append step of w like the HBM-bound attention workloads:
+    cold, cycling through `copies` input copies (default COLD_FOOTPRINT worth),
+    and warm on one. Returns (result dict, copies used, AppendInputs)."""
+    from workloads.device import AppendInputs
+    ai = AppendInputs(w, "cuda:0")
+    nbytes = append_bytes(ai)
+    if copies is None:
+        copies = max(1, min(64, -(-COLD_FOOTPRINT // nbytes)))
+
+    def rate(ms):
+        t = ms / 1e3
+        gbs = nbytes / t / 1e9
+        return {"ms_per_step": round(ms, 6), "gbs": round(gbs, 2), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "tokens_per_s": round(ai.n_tokens / t, 1), "bytes": nbytes}
+
+    ms_warm, ms_eager, per_graph = time_steps([ai], steps, warmup, graph_launches, {}, 0)
+    res = {"bound": "hbm", "copies": copies, "eager_ms_per_step": ms_eager, "launches_per_graph": per_graph}
+    if copies > 1:
+        ais = [ai] + [AppendInputs(w, "cuda:0") for _ in range(copies - 1)]
+        ms_cold, _, per_graph = time_steps(ais, steps, warmup, graph_launches, {}, 0)
+        res.update(rate(ms_cold))
+        res["warm"] = rate(ms_warm)
+        del ais
+    else:
+        res.update(rate(ms_warm))
+    res["frac"] = res["hbm_frac"]
+    return res, copies, ai
+
+
+def append_entry(ai, r) -> dict:
+    e = {"workload": APPEND_NAME, "source": ai.w.name, "dtype": ai.w.dtype, "bound": "hbm",
+         "frac": r["frac"], "ms_per_step": r["ms_per_step"], "gbs": r["gbs"], "tokens_per_s": r["tokens_per_s"],
+         "hbm_frac": r["hbm_frac"], "timing": timing_label(r), "kernel": kernel_name(APPEND_NAME)}
+    if "warm" in r:
+        e["warm"] = {k: r["warm"][k] for k in ("ms_per_step", "gbs", "hbm_frac")}
+    return e
+
+
+def append_main(args):
+    """bench.py --config kv_append: one JSON line for the append step alone."""
+    import torch
+    from workloads import make_config
+    w = make_config(APPEND_SOURCE)
+    r, copies, ai = measure_append(w, args.steps, args.warmup, args.graph_launches, args.copies)
+    torch.cuda.synchronize()
+    log("[bench] %s: %d steps, %.5f ms/step" % (APPEND_NAME, args.steps, r["ms_per_step"]))
+    line = {
+        "metric": "paged KV append GB/s (new K/V rows read and written once)", "value": r["gbs"],
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "f16" else "bf16", "data": "synthetic", "config": append_summary(ai),
+        "tokens_per_s": r["tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": r["hbm_frac"], "traffic": measured_traffic(APPEND_NAME),
+                     "algorithmic_bytes": r["bytes"], "algorithmic_flops": 0,
+                     "kernel": kernel_name(APPEND_NAME)},
+        "timing": {"mode": "hip_graph_replay" if args.graph_launches > 0 else "eager",
+                   "launches_per_graph": r["launches_per_graph"], "input_copies": copies,
+                   "inputs": timing_label(r)},
+        "cpu_baseline": None,
+    }
+    if "warm" in r:
+        line["warm"] = r["warm"]
+    print(json.dumps(line), flush=True)
+
+
 def config_summary(w) -> dict:
     qo = np.diff(w.q_indptr)
     c = {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
@@ -230,6 +330,8 @@ def config_summary(w) -> dict:
 
 def kernel_name(workload: str) -> str:
     """The dominant kernel of a workload's step."""
+    if workload == APPEND_NAME:
+        return "kv_append_kernel"
     return "mla_fwd_kernel" if workload.startswith("mla") else KERNEL_NAME
 
 
@@ -262,7 +364,7 @@ def source_code_text(text: str) -> str:
 def kernel_source_hash(kernel: str = KERNEL_NAME) -> str:
     """Hash of the kernel's code (comments and layout excluded): a counter
     summary in profiles/ applies while it matches."""
-    src = "mla_fwd.hip" if kernel == "mla_fwd_kernel" else "attn_fwd.hip"
+    src = {"mla_fwd_kernel": "mla_fwd.hip", "kv_append_kernel": "kv_append.hip"}.get(kernel, "attn_fwd.hip")
     h = hashlib.sha256()
     for name in (src, "device_common.h", "ra_internal.h"):
         with open(os.path.join(ROOT, "attention_ragged_gqa_amd", "csrc", name), encoding="utf-8") as f:
@@ -482,7 +584,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=str(DEFAULT_CONFIG),
-                    help="0..4, or an extra workload name (paged_decode, ragged_left_padded)")
+                    help="0..4, or an extra workload name (paged_decode, ragged_left_padded, "
+                         "mla_prefill, kv_append)")
     ap.add_argument("--split", type=int, default=None,
                     help="split-KV count for paged workloads (0: auto, -1: unsplit entry point); "
                          "default: auto for paged_decode, unsplit otherwise")
@@ -518,6 +621,9 @@ def main():
     from workloads import CONFIG_NAMES, EXTRA_NAMES, make_config, make_extra
 
     ra.library()
+    if args.config == APPEND_NAME:
+        append_main(args)
+        return
     if args.waves is not None:
         ra.ra_set_workgroup_waves(args.waves)
     t_gen = time.perf_counter()
@@ -604,6 +710,14 @@ def main():
                 % (we.name, re_["ms_per_step"], re_["bound"], re_["frac"], time.perf_counter() - t0))
             del we
             torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        wa = make_config(APPEND_SOURCE) if str(APPEND_SOURCE) != args.config else w
+        ra_, _, ai = measure_append(wa, APPEND_STEPS, 5, args.graph_launches)
+        extra.append(append_entry(ai, ra_))
+        log("[bench] extra %s: %.5f ms/step, hbm frac %.4f (%.1fs)"
+            % (APPEND_NAME, ra_["ms_per_step"], ra_["frac"], time.perf_counter() - t0))
+        del ai
+        torch.cuda.empty_cache()
         line["extra_workloads"] = extra
 
     if not args.no_cpu_baseline:

@@ -161,3 +161,19 @@ def test_timing_label_by_input_footprint():
     assert bench.timing_label({"copies": 26, "bytes": 21 << 20}) == "cold (26 input copies cycled)"
     assert bench.timing_label({"copies": 1, "bytes": 1 << 30}).startswith("one copy of 1024 MB, larger than")
     assert bench.timing_label({"copies": 1, "bytes": 100 << 20}) == "warm"
+
+
+def test_append_bytes_closed_form():
+    """Two sequences whose new tokens start mid-page: 5 tokens at storage
+    offsets 15..19 (pages 0 and 1 of the sequence) and 17 at 23..39 (pages 1
+    and 2). Each new token's K and V rows are read once and written once;
+    int32 positions, append indptr (b + 1), starts (b), page indptr (b + 1)
+    and the 4 page-table entries touched."""
+    from types import SimpleNamespace
+    w = make_custom_paged(5, [5, 17], [20, 40], h_q=4, h_kv=2, d=64, dtype="bf16", causal=1,
+                          store_rope="linear")
+    ai = SimpleNamespace(w=w, n_tokens=22, new_start=np.array([15, 23]), new_len=np.array([5, 17]))
+    row = 2 * 64 * 2
+    assert bench.append_bytes(ai) == 4 * 22 * row + 4 * 22 + 4 * 3 + 4 * 2 + 4 * 3 + 4 * 4
+    assert bench.kernel_name(bench.APPEND_NAME) == "kv_append_kernel"
+    assert bench.kernel_source_hash("kv_append_kernel") != bench.kernel_source_hash("attn_fwd_kernel")

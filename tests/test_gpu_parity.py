@@ -229,6 +229,72 @@ def test_append_matches_oracle_rope(dtype, d):
     assert n_diff == 0, "%d rotated K values differ from the oracle" % n_diff
 
 
+@pytest.mark.parametrize("h_kv,d,batch", [(3, 128, 6), (1, 64, 9), (40, 128, 5), (64, 64, 3), (2, 128, 1500)])
+def test_append_shapes(h_kv, d, batch):
+    """The append kernel's token-to-workgroup shapes (a thread per 16-byte
+    chunk pair, 256 threads): several tokens per workgroup with a pair count
+    that does not divide it (h_kv 3, d 128: ten tokens of 24 pairs), many
+    (h_kv 1, d 64: 64 tokens), one token of exactly 256 pairs (h_kv 64, d 64),
+    one wider than the workgroup (h_kv 40, d 128: 320 pairs, looped over),
+    and a batch of 1,500 sequences whose index arrays do not fit the LDS copy
+    (searched in global memory). Prefix appended, then the new tokens
+    mid-page; the whole pool against the oracle's rotation, bit-identical,
+    unused slots zero."""
+    from tests.parity import gpu_pages
+    from workloads import pages_from_logical
+    rng = np.random.default_rng(9900 + h_kv)
+    qo = [int(x) for x in rng.integers(1, 40 if batch < 100 else 4, size=batch)]
+    stored = [q + int(rng.integers(0, 70 if batch < 100 else 30)) for q in qo]
+    w = make_custom_paged(9900 + h_kv, qo, stored, h_q=h_kv, h_kv=h_kv, d=d, dtype="bf16", causal=1,
+                          store_rope="linear", rope_theta=1e4)
+    say("[gpu] append shapes h_kv=%d d=%d batch=%d: %d tokens" % (h_kv, d, batch, sum(stored)))
+    pool = gpu_pages(w, "cuda:0")
+    torch.cuda.synchronize()
+    ref = pages_from_logical(w)
+    w.k_store = torch.from_numpy(oracle.rope(w.k_store, w.store_rope_position, 1e4, 1.0, "bf16")).to(w.q.dtype)
+    ref_rot = pages_from_logical(w)
+    got = pool.cpu()
+    assert torch.equal(got[:, 1], ref[:, 1]), "V"
+    n_diff = int((got[:, 0] != ref_rot[:, 0]).sum())
+    assert n_diff == 0, "%d rotated K values differ from the oracle" % n_diff
+
+
+def test_append_workload_full_size():
+    """The benchmark's append step at full size: spec_tree_paged's 32,768 new
+    tree tokens (K rotated at prefix + depth, theta 5e5) appended twice into
+    its 2.3 GB paged cache, after the 4,096-token prefixes. Every new token's
+    page slot against the oracle's rotation (bit-identical K, V copied
+    exactly), and every other value of the pool unchanged."""
+    from workloads.device import AppendInputs
+    w = make_config(4)
+    ai = AppendInputs(w)
+    before = ai.pool.clone()
+    say("[gpu] append workload: %d tokens into %d pages" % (ai.n_tokens, w.num_pages))
+    ai.launch()
+    ai.launch()
+    torch.cuda.synchronize()
+    pages, slots, idx = [], [], []
+    for b in range(w.batch):
+        off = ai.new_start[b] + np.arange(ai.new_len[b])
+        pages.append(w.page_values[w.page_indptr[b] + off // 16])
+        slots.append(off % 16)
+        idx.append(int(w.kv_store_indptr[b]) + off)
+    pg = torch.from_numpy(np.concatenate(pages).astype(np.int64)).cuda()
+    sl = torch.from_numpy(np.concatenate(slots).astype(np.int64)).cuda()
+    idx = np.concatenate(idx).astype(np.int64)
+    got_k = ai.pool[pg, 0, :, sl, :].cpu()                  # [n, h_kv, d]
+    got_v = ai.pool[pg, 1, :, sl, :].cpu()
+    ref_k = torch.from_numpy(oracle.rope(w.k_store[idx], np.asarray(w.store_rope_position)[idx],
+                                         w.rope_theta, w.rope_scale, w.dtype)).to(w.q.dtype)
+    assert torch.equal(got_v, w.v_store[idx]), "V not copied exactly"
+    n_diff = int((got_k != ref_k).sum())
+    assert n_diff == 0, "%d of %d rotated K values differ from the oracle" % (n_diff, got_k.numel())
+    before[pg, :, :, sl, :] = ai.pool[pg, :, :, sl, :]
+    assert torch.equal(ai.pool, before), "values outside the new tokens' slots changed"
+    del ai, before
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,d,theta,scale", [("bf16", 128, 5e5, 1.0), ("f16", 64, 1e4, 0.5)])
 def test_rotation_bit_exact_at_scale(dtype, d, theta, scale):
     """Two million values rotated by the append kernel (positions up to

@@ -146,3 +146,47 @@ class DeviceInputs:
                                 tree_order=self.tree_order, causal=w.causal, out=self.out,
                                 lse=self.lse, rotary_mode=w.rotary_mode, rope_scale=w.rope_scale,
                                 rope_theta=w.rope_theta, sm_scale=w.sm_scale, stream=stream)
+
+
+class AppendInputs:
+    """The append step of a paged workload whose K is rotated before caching:
+    the new tokens of every sequence (its last qo_len stored tokens, K, V and
+    their cache positions, on the device) and the page pool. launch() appends
+    the new tokens at their storage offsets (after each sequence's cached
+    prefix, mid-page where the prefix ends mid-page), rotating K; repeated
+    launches rewrite the same values. The append never reads the pool, so
+    the prefix slots are left zero (staging them would run the same kernel
+    on 16 times the tokens of the measured step)."""
+
+    def __init__(self, w, dev="cuda:0"):
+        if w.kind != "paged" or w.store_rope_position is None:
+            raise ValueError("the append step needs a paged workload with K rotated before caching")
+        self.w = w
+        self.dev = torch.device(dev)
+        d = self.dev
+        stored = np.diff(w.kv_store_indptr).astype(np.int64)
+        new = np.minimum(np.diff(w.q_indptr).astype(np.int64), stored)
+        old = stored - new
+        self.n_tokens = int(new.sum())
+        self.pool = torch.zeros((w.num_pages, 2, w.h_kv, 16, w.d), dtype=w.q.dtype, device=d)
+        idx = np.concatenate([np.arange(int(w.kv_store_indptr[b]) + old[b], int(w.kv_store_indptr[b + 1]))
+                              for b in range(w.batch)]).astype(np.int64)
+        sel = torch.from_numpy(idx)
+        self.k = w.k_store[sel].to(d)
+        self.v = w.v_store[sel].to(d)
+        indptr = np.zeros(w.batch + 1, np.int64)
+        indptr[1:] = np.cumsum(new)
+        self.append_indptr = _i32(indptr, d)
+        self.append_start = _i32(old, d)
+        self.rope_position = _i32(np.asarray(w.store_rope_position)[idx], d)
+        self.page_indptr = _i32(w.page_indptr, d)
+        self.page_values = _i32(w.page_values, d)
+        self.new_start = old
+        self.new_len = new
+
+    def launch(self, stream=None):
+        import attention_ragged_gqa_amd as ra
+        w = self.w
+        return ra.ra_paged_kv_append(self.k, self.v, self.append_indptr, self.append_start,
+                                     self.rope_position, self.page_indptr, self.page_values, self.pool,
+                                     rope_scale=w.rope_scale, rope_theta=w.rope_theta, stream=stream)

@@ -5,11 +5,11 @@
 //
 // A workgroup of 256 threads handles a group of T = 256 / (h_kv * D/16)
 // consecutive tokens at a time (one when a token has more chunk pairs than
-// threads; its pairs are then looped over). A thread holds one 16-byte chunk of a head row's first
-// half and its RoPE partner in the second half (dims +- D/2), for K and for
-// V, so the rotation needs no cross-lane exchange; the pairs of a token sit
-// on consecutive threads, and each wave-wide load or store covers 128-byte
-// runs of the head rows.
+// threads; its pairs are then looped over). A thread holds one 16-byte
+// chunk of a head row's first half and its RoPE partner in the second half
+// (dims +- D/2), for K and for V, so the rotation needs no cross-lane
+// exchange; the pairs of a token sit on consecutive threads, and each
+// wave-wide load or store covers 128-byte runs of the head rows.
 //
 // The grid holds at most eight workgroups per compute unit of the MI355X
 // (2048); each loads the batch's append_indptr, page_indptr and

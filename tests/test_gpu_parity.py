@@ -691,6 +691,50 @@ def test_ragged_left_padded_workload():
     _check(w, w.name)
 
 
+@pytest.mark.parametrize("kind,dtype,waves", [("ragged", "bf16", 0), ("ragged", "f16", 8),
+                                               ("paged", "bf16", 0), ("paged", "bf16", 8)])
+def test_uniform_scores_are_prefix_means(kind, dtype, waves):
+    """All scores equal (q = 0): every weight is 1, so under the causal mask
+    out[t] is the mean of the first lim_t V rows of the chunk, lim_t =
+    L - qo + t + 1, and lse = log2(lim_t): a closed form from a float64
+    cumulative sum, independent of the oracle. 130 and 70 queries over 1,000
+    and 70 keys (ties in every row maximum, up to 1,000 equal weights)."""
+    import attention_ragged_gqa_amd as ra
+    if kind == "ragged":
+        w = make_custom_ragged(9950, [130, 70], [1000, 70], h_q=8, h_kv=2, d=128, dtype=dtype, causal=1,
+                               name="uniform_ragged")
+        vs = [w.v[int(w.kv_indptr[b]):int(w.kv_indptr[b + 1])] for b in range(w.batch)]
+    else:
+        w = make_custom_paged(9951, [130, 70], [1000, 70], h_q=8, h_kv=2, d=128, dtype=dtype, causal=1,
+                              name="uniform_paged")
+        vs = [w.v_store[int(w.kv_store_indptr[b]):int(w.kv_store_indptr[b + 1])] for b in range(w.batch)]
+    w.q.zero_()
+    ra.ra_set_workgroup_waves(waves)
+    try:
+        di = DeviceInputs(w)
+        di.poison()
+        out, lse = di.launch()
+        torch.cuda.synchronize()
+    finally:
+        ra.ra_set_workgroup_waves(0)
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    g = w.h_q // w.h_kv
+    for b in range(w.batch):
+        q0, qo = int(w.q_indptr[b]), int(w.q_indptr[b + 1]) - int(w.q_indptr[b])
+        vb = vs[b].double().numpy()                                   # [L, h_kv, d]
+        L = vb.shape[0]
+        csum = np.cumsum(vb, axis=0)
+        lim = L - qo + np.arange(qo) + 1                              # >= 1 here
+        ref = csum[lim - 1] / lim[:, None, None]                      # [qo, h_kv, d]
+        ref = np.repeat(ref, g, axis=1)                               # query head h reads h // g
+        tol = 2e-3 + np.abs(ref) * (2.0 ** -8 if dtype == "bf16" else 2.0 ** -11)
+        err = np.abs(out[q0:q0 + qo] - ref)
+        assert np.all(err <= tol), "seq %d: max |d out| %.3g" % (b, err.max())
+        lse_ref = np.log2(lim.astype(np.float64))[:, None]
+        assert np.allclose(lse[q0:q0 + qo], lse_ref, rtol=1e-6, atol=1e-6), "seq %d lse" % b
+    say("[gpu] uniform scores %s %s waves %d: prefix means and log2 counts hold" % (kind, dtype, waves))
+
+
 # ---------------------------------------------------------------------------
 # the running softmax reference moving after the first tile
 # ---------------------------------------------------------------------------

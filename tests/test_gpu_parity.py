@@ -146,7 +146,13 @@ def test_tree_chain_and_singletons():
     w.tree_mask = np.concatenate([
         np.stack([np.arange(70), np.full(70, 70)], axis=1),          # chain: node i ancestor of all later
         np.stack([np.arange(40), np.arange(1, 41)], axis=1)]).astype(np.int32)
-    _check(w, "tree_chain_singletons")
+    di = _check(w, "tree_chain_singletons")
+    # a node that sees only itself has the single weight 1: its output is its
+    # own V row bit for bit (every singleton, and the chain's root)
+    g = w.h_q // w.h_kv
+    own = torch.cat([w.v[0:1], w.v[70:110]]).repeat_interleave(g, dim=1)
+    got = torch.cat([di.out[0:1], di.out[70:110]]).cpu()
+    assert torch.equal(got, own), "a one-key row differs from its V row"
 
 
 # ---------------------------------------------------------------------------

@@ -697,6 +697,71 @@ def test_ragged_left_padded_workload():
     _check(w, w.name)
 
 
+def test_invariances_bit_exact():
+    """Metamorphic checks, no oracle: a row's arithmetic (its tiles in order,
+    tiles without a visible key adding exact zeros) does not depend on how
+    rows are packed or where pages live, so these hold bit for bit. Paged
+    causal bf16 with inline q RoPE over a cache rotated when appended:
+    (a) GQA with g = 4 equals the same K/V replicated to g = 1;
+    (b) a permuted page table over a permuted pool equals the original;
+    (c) each sequence run on its own equals its rows of the batched run;
+    (d) four-wave and eight-wave workgroups give the same bits."""
+    import copy
+    w = make_custom_paged(9960, [70, 130, 9], [300, 130, 500], h_q=8, h_kv=2, d=128, dtype="bf16",
+                          causal=1, store_rope="linear", rotary_mode=1, rope_theta=1e4, name="invariance")
+    di = DeviceInputs(w)
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    out, lse = out.clone(), lse.clone()
+    g = w.h_q // w.h_kv
+    # (a) replicated K/V, one query head per KV head
+    wr = copy.copy(w)
+    wr.h_kv = w.h_q
+    wr.k_store = w.k_store.repeat_interleave(g, dim=1)
+    wr.v_store = w.v_store.repeat_interleave(g, dim=1)
+    out_r, lse_r = DeviceInputs(wr).launch()
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out) and torch.equal(lse_r, lse), "GQA differs from replicated KV"
+    # (b) pages moved: pool2[perm[p]] = pool[p], page_values2 = perm[page_values]
+    perm = torch.from_numpy(np.random.default_rng(9961).permutation(w.num_pages)).cuda()
+    di2 = DeviceInputs(w)
+    pool2 = torch.empty_like(di2.pages)
+    pool2[perm] = di2.pages
+    di2.pages = pool2
+    di2.page_values = perm[di2.page_values.long()].to(torch.int32)
+    out_p, lse_p = di2.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out) and torch.equal(lse_p, lse), "page permutation changes the result"
+    # (c) one sequence at a time
+    for b in range(w.batch):
+        q0, q1 = int(w.q_indptr[b]), int(w.q_indptr[b + 1])
+        p0, p1 = int(w.page_indptr[b]), int(w.page_indptr[b + 1])
+        dd = DeviceInputs(w)
+        dd.q = di.q[q0:q1].contiguous()
+        dd.q_indptr = torch.tensor([0, q1 - q0], dtype=torch.int32, device="cuda")
+        dd.q_rope_position = di.q_rope_position[q0:q1].contiguous()
+        dd.page_indptr = torch.tensor([0, p1 - p0], dtype=torch.int32, device="cuda")
+        dd.page_values = di.page_values[p0:p1].contiguous()
+        dd.length_info = di.length_info[b:b + 1].contiguous()
+        dd.out = torch.empty_like(dd.out[q0:q1])
+        dd.lse = torch.empty_like(dd.lse[q0:q1])
+        o1, l1 = dd.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[q0:q1]) and torch.equal(l1, lse[q0:q1]), "sequence %d alone differs" % b
+    # (d) both workgroup shapes
+    import attention_ragged_gqa_amd as ra
+    try:
+        for n in (4, 8):
+            ra.ra_set_workgroup_waves(n)
+            o_n, l_n = di.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(o_n, out) and torch.equal(l_n, lse), "%d waves differ" % n
+    finally:
+        ra.ra_set_workgroup_waves(0)
+    say("[gpu] invariances: GQA = replicated KV, page permutation, per-sequence runs, "
+        "workgroup shapes: bit-identical")
+
+
 @pytest.mark.parametrize("kind,dtype,waves", [("ragged", "bf16", 0), ("ragged", "f16", 8),
                                                ("paged", "bf16", 0), ("paged", "bf16", 8)])
 def test_uniform_scores_are_prefix_means(kind, dtype, waves):

@@ -762,6 +762,38 @@ def test_invariances_bit_exact():
         "workgroup shapes: bit-identical")
 
 
+def test_invariances_across_entry_points():
+    """Bit for bit, no oracle: (e) tree attention over chains (every node the
+    child of the previous one) equals causal ragged prefill on the same
+    q/k/v, the tree test and the causal bound selecting the same keys;
+    (f) causal attention over contiguous K/V equals the paged entry point
+    over the same tokens behind a permuted page table (fp16 and bf16)."""
+    import attention_ragged_gqa_amd as ra
+    for dtype in ("f16", "bf16"):
+        # (e) chains of 150 and 77 nodes, d 64, h 8/2
+        w = make_custom_tree(9970, [150, 77], h_q=8, h_kv=2, d=64, dtype=dtype, name="chains")
+        w.tree_mask = np.concatenate([np.stack([np.arange(n), np.full(n, n)], axis=1)
+                                      for n in (150, 77)]).astype(np.int32)
+        di = DeviceInputs(w)
+        out_t, lse_t = di.launch()
+        out_c, lse_c = ra.ra_ragged_prefill(di.q, di.q_indptr, di.k, di.v, di.kv_indptr, causal=1,
+                                            sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_t, out_c) and torch.equal(lse_t, lse_c), "%s: chain tree != causal" % dtype
+        # (f) the same tokens contiguous and paged, 60 and 200 queries over 333 and 200 keys
+        wp = make_custom_paged(9971, [60, 200], [333, 200], h_q=16, h_kv=4, d=128, dtype=dtype, causal=1,
+                               name="contiguous_vs_paged")
+        dp = DeviceInputs(wp)
+        out_p, lse_p = dp.launch()
+        k = wp.k_store.cuda()
+        v = wp.v_store.cuda()
+        kv_indptr = torch.from_numpy(wp.kv_store_indptr.astype(np.int32)).cuda()
+        out_r, lse_r = ra.ra_ragged_prefill(dp.q, dp.q_indptr, k, v, kv_indptr, causal=1, sm_scale=wp.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_p, out_r) and torch.equal(lse_p, lse_r), "%s: paged != contiguous" % dtype
+    say("[gpu] invariances across entry points: chain tree = causal, paged = contiguous: bit-identical")
+
+
 @pytest.mark.parametrize("kind,dtype,waves", [("ragged", "bf16", 0), ("ragged", "f16", 8),
                                                ("paged", "bf16", 0), ("paged", "bf16", 8)])
 def test_uniform_scores_are_prefix_means(kind, dtype, waves):

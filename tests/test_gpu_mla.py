@@ -143,3 +143,34 @@ def test_mla_page_pool_beyond_4gib():
     torch.cuda.synchronize()
     d_out, d_lse = compare(out, lse, ref[0], ref[1], label="latent pool beyond 4 GiB")
     say("[gpu] latent pool beyond 4 GiB: max|d out| %.2e max rel|d lse| %.2e" % (d_out, d_lse))
+
+
+def test_mla_invariances_bit_exact():
+    """No oracle: a permuted page table over a permuted latent pool, and each
+    sequence run on its own, give the batched run's bits (bf16, causal)."""
+    import attention_ragged_gqa_amd as ra
+    w = make_custom_mla(9980, [70, 129, 5], [300, 129, 400], h_q=16, d_qk=576, d_latent=512, dtype="bf16",
+                        causal=1)
+    di = DeviceInputs(w)
+    out, lse = di.launch()
+    torch.cuda.synchronize()
+    out, lse = out.clone(), lse.clone()
+    perm = torch.from_numpy(np.random.default_rng(9981).permutation(w.num_pages)).cuda()
+    pool = torch.empty_like(di.pages)
+    pool[perm] = di.pages
+    o_p, l_p = ra.ra_mla_paged_prefill(di.q, di.q_indptr, pool, di.page_indptr,
+                                       perm[di.page_values.long()].to(torch.int32), di.length_info,
+                                       causal=1, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, out) and torch.equal(l_p, lse), "page permutation changes the result"
+    for b in range(w.batch):
+        q0, q1 = int(w.q_indptr[b]), int(w.q_indptr[b + 1])
+        p0, p1 = int(w.page_indptr[b]), int(w.page_indptr[b + 1])
+        o1, l1 = ra.ra_mla_paged_prefill(di.q[q0:q1].contiguous(),
+                                         torch.tensor([0, q1 - q0], dtype=torch.int32, device="cuda"),
+                                         di.pages, torch.tensor([0, p1 - p0], dtype=torch.int32, device="cuda"),
+                                         di.page_values[p0:p1].contiguous(), di.length_info[b:b + 1].contiguous(),
+                                         causal=1, sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[q0:q1]) and torch.equal(l1, lse[q0:q1]), "sequence %d alone differs" % b
+    say("[gpu] latent invariances: page permutation and per-sequence runs bit-identical")

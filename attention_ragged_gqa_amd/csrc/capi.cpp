@@ -516,6 +516,9 @@ ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append
   if (dtype != RA_F16 && dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "dtype %d not supported", (int)dtype);
   if (head_dim != 64 && head_dim != 128) return fail(RA_EUNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
   if (page_size != 16) return fail(RA_EUNSUPPORTED, "page_size %d not supported (16)", page_size);
+  // the kernel's token and chunk indices are 32-bit
+  if (n_tokens > (1 << 30) || h_kv > (1 << 16))
+    return fail(RA_EUNSUPPORTED, "n_tokens %d or h_kv %d past the kernel's limits (2^30, 2^16)", n_tokens, h_kv);
   if (n_tokens == 0) return ok();
   if (k == nullptr || v == nullptr || append_indptr == nullptr || append_start == nullptr ||
       page_indptr == nullptr || pages == nullptr || (nnz_pages > 0 && page_values == nullptr))

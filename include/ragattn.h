@@ -294,6 +294,10 @@ ra_status ra_mla_paged_prefill(const void* q, const int32_t* q_indptr, const voi
  * of pages [num_pages, 2, h_kv, page_size, head_dim]. K is rotated at
  * rope_position[token] with the angles of ra_tree_attn. A token whose page
  * index falls outside page_values or the pool is skipped.
+ * Errors: RA_EINVAL (negative sizes, tokens without sequences, NULL
+ * pointers, non-finite rope_theta/rope_scale with rotation), RA_EUNSUPPORTED
+ * (head_dim not 64/128, dtype, page size not 16, n_tokens > 2^30 or
+ * h_kv > 2^16), RA_EHIP (launch error).
  */
 ra_status ra_paged_kv_append(const void* k, const void* v, const int32_t* append_indptr,
                              const int32_t* append_start, const int32_t* rope_position,

@@ -578,6 +578,8 @@ void append_checks() {
   { Append p; p.page_size = 64; cases.push_back({"page_size", p, RA_EUNSUPPORTED}); }
   { Append p; p.h_kv = -2; cases.push_back({"h_kv", p, RA_EINVAL}); }
   { Append p; p.n_tokens = -1; cases.push_back({"n_tokens", p, RA_EINVAL}); }
+  { Append p; p.n_tokens = (1 << 30) + 1; cases.push_back({"n_tokens limit", p, RA_EUNSUPPORTED}); }
+  { Append p; p.h_kv = (1 << 16) + 1; cases.push_back({"h_kv limit", p, RA_EUNSUPPORTED}); }
   for (const Case& c : cases) {
     stub_reset();
     const ra_status st = c.p.call();

@@ -265,6 +265,32 @@ def test_append_shapes(h_kv, d, batch):
     assert n_diff == 0, "%d rotated K values differ from the oracle" % n_diff
 
 
+@pytest.mark.parametrize("h_kv,d,dtype", [(2, 128, "bf16"), (3, 64, "f16"), (40, 128, "bf16")])
+def test_append_without_rotation(h_kv, d, dtype):
+    """rope_position NULL: K and V copied as they are. Prefix, then the new
+    tokens mid-page, in two calls; the whole pool equals the pages built
+    on the host from the same tokens, bit for bit (unused slots zero)."""
+    from workloads import pages_from_logical
+    import attention_ragged_gqa_amd as ra
+    w = make_custom_paged(9990 + h_kv, [7, 30, 1], [40, 95, 17], h_q=h_kv, h_kv=h_kv, d=d, dtype=dtype,
+                          causal=1)
+    pool = torch.zeros((w.num_pages, 2, w.h_kv, 16, w.d), dtype=w.q.dtype, device="cuda")
+    stored = np.diff(w.kv_store_indptr).astype(np.int64)
+    new = np.minimum(np.diff(w.q_indptr).astype(np.int64), stored)
+    for starts, lens in ((np.zeros(w.batch, np.int64), stored - new), (stored - new, new)):
+        idx = np.concatenate([np.arange(int(w.kv_store_indptr[b]) + starts[b],
+                                        int(w.kv_store_indptr[b]) + starts[b] + lens[b])
+                              for b in range(w.batch)]).astype(np.int64)
+        sel = torch.from_numpy(idx)
+        indptr = np.zeros(w.batch + 1, np.int64)
+        indptr[1:] = np.cumsum(lens)
+        i32 = lambda a: torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device="cuda")
+        ra.ra_paged_kv_append(w.k_store[sel].cuda(), w.v_store[sel].cuda(), i32(indptr), i32(starts), None,
+                              i32(w.page_indptr), i32(w.page_values), pool)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.cpu(), pages_from_logical(w)), "unrotated append differs from the host pages"
+
+
 def test_append_workload_full_size():
     """The benchmark's append step at full size: spec_tree_paged's 32,768 new
     tree tokens (K rotated at prefix + depth, theta 5e5) appended twice into

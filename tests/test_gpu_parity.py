@@ -197,6 +197,12 @@ PAGED_CASES = [
          rope_theta=5e5, rope_scale=0.25, sm_scale=0.15),
     dict(seed=28, qo=[77, 5], stored=[500, 333], h_q=8, h_kv=2, d=64, dtype="f16", causal=1,
          store_rope="linear", rope_scale=0.5, sm_scale=0.3, sliding=None),
+    # in-kernel K rotation with a tree mask, and with a sliding window + sink
+    # (K at chunk position j rotated at k_rope_pos_offset[b] + j)
+    dict(seed=29, qo=[40, 90], stored=[200, 90], h_q=16, h_kv=4, d=128, dtype="bf16", causal=0,
+         tree=True, tree_max_children=3, rotary_mode=1, k_rope_pos_offset=[11, 3000]),
+    dict(seed=30, qo=[20, 60], stored=[700, 300], h_q=8, h_kv=2, d=64, dtype="f16", causal=1,
+         sliding=([500, 130], [4, 0]), rotary_mode=1, k_rope_pos_offset=[0, 77]),
 ]
 
 
